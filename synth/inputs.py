@@ -1,0 +1,109 @@
+"""Workload table and seeded input generators.
+
+Values are drawn N(0, 1) in float32 on the CPU with ``torch.Generator`` seeded
+as ``1000 * workload_id + {0: q, 1: k, 2: v}``, so the oracle and the GPU see
+identical numbers. Storage formats:
+
+* "bf16": round-to-nearest-even through ``tensor.to(torch.bfloat16)``;
+  returned as uint16 bit patterns.
+* "e4m3fn": per-tensor amax scaling, descale = amax / 448 (1 when amax = 0),
+  codes = e4m3fn(x / descale) through ``torch.float8_e4m3fn`` (round to nearest
+  even, clamped to +/-448 first); returned as uint8 codes plus the float32
+  descale. The +/-448 range is the e4m3fn range given on the page "[ops] feat:
+  run the DeepSeek-V4 TileLang kernels and FP8 QAT on AMD gfx942/gfx950"; the
+  amax rule is the plainest reading of "per-tensor amax scales".
+
+The shapes are the five workloads of the attention forward: a tiny fp32 case,
+an LLM-style case, the video-DiT self-attention (bf16 and fp8) and a GQA causal
+case that is also run as two key chunks. The video-DiT shape is the one the
+page "F8 fmha ASM gfx950" benchmarks (b 1, n 5, q 75600, d 128).
+"""
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    wid: int
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Skv: int
+    D: int
+    fmt: str                     # "f32" (tiny case, rounded to bf16 for the GPU), "bf16", "e4m3fn"
+    causal: tuple = (False,)
+    chunks: tuple = ()           # key chunk lengths for the chunked-merge run
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def flops(self, causal: bool) -> float:
+        """4*B*Hq*Sq*Skv*D, halved for causal (the metric's own convention)."""
+        f = 4.0 * self.B * self.Hq * self.Sq * self.Skv * self.D
+        return f / 2 if causal else f
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload(1, "tiny", 1, 2, 2, 256, 256, 64, "f32", (False,),
+                 note="fp32 N(0,1), scale 1/sqrt(64), non-causal"),
+        Workload(2, "llm", 2, 8, 8, 2048, 2048, 128, "bf16", (False, True)),
+        Workload(3, "video_dit", 1, 5, 5, 75600, 75600, 128, "bf16", (False,)),
+        Workload(4, "video_dit_fp8", 1, 5, 5, 75600, 75600, 128, "e4m3fn", (False,)),
+        Workload(5, "gqa_causal", 1, 32, 8, 8192, 8192, 128, "bf16", (True,), chunks=(4096, 4096)),
+    ]
+}
+
+
+def normal(shape, seed: int) -> torch.Tensor:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+
+def to_bf16_bits(x: torch.Tensor) -> np.ndarray:
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def quant_e4m3fn_per_tensor(x: torch.Tensor):
+    """-> (uint8 codes, float32 descale) with x ~= decode(codes) * descale."""
+    amax = float(x.abs().max()) if x.numel() else 0.0
+    descale = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    y = (x / torch.tensor(float(descale), dtype=torch.float32)).clamp(-448.0, 448.0)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, descale
+
+
+def make_inputs(w: Workload, fmt: str = None, sq: int = None, skv: int = None):
+    """Draw q, k, v for workload ``w`` (optionally with shorter Sq / Skv).
+
+    Returns a dict with ``fmt`` ("bf16" or "e4m3fn"), the stored arrays ``q``,
+    ``k``, ``v`` (uint16 bf16 bits or uint8 e4m3fn codes), the descales (1.0 for
+    bf16) and ``q32``/``k32``/``v32``, the float32 draws before rounding.
+    """
+    fmt = fmt or ("bf16" if w.fmt in ("f32", "bf16") else w.fmt)
+    Sq = sq if sq is not None else w.Sq
+    Skv = skv if skv is not None else w.Skv
+    base = 1000 * w.wid
+    q32 = normal((w.B, w.Hq, Sq, w.D), base + 0)
+    k32 = normal((w.B, w.Hkv, Skv, w.D), base + 1)
+    v32 = normal((w.B, w.Hkv, Skv, w.D), base + 2)
+    out = dict(fmt=fmt, q32=q32, k32=k32, v32=v32)
+    if fmt == "bf16":
+        out.update(q=to_bf16_bits(q32), k=to_bf16_bits(k32), v=to_bf16_bits(v32),
+                   q_descale=1.0, k_descale=1.0, v_descale=1.0)
+    elif fmt == "e4m3fn":
+        (qc, qd), (kc, kd), (vc, vd) = (quant_e4m3fn_per_tensor(t) for t in (q32, k32, v32))
+        out.update(q=qc, k=kc, v=vc, q_descale=float(qd), k_descale=float(kd), v_descale=float(vd))
+    else:
+        raise ValueError(fmt)
+    return out
