@@ -1,0 +1,157 @@
+"""Python binding of the gfx950 fused attention forward (``libattn.so``).
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels behind the C ABI declared in ``include/attn.h``. The functions
+``attn_fwd``, ``attn_fwd_chunk``, ``attn_merge_lse2_host`` and
+``attn_status_string`` carry the C names and arguments one for one (pointer
+arguments accept a torch tensor, a plain integer address or None) and return
+the C status code. ``forward`` is a convenience wrapper over ``attn_fwd_chunk``
+that reads the sizes off torch tensors, allocates the outputs with torch and
+raises ``AttnError`` on a non-OK status.
+
+There is no fallback: if the library is missing, loading raises.
+"""
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "ATTN_BF16", "ATTN_FP8_E4M3FN", "STATUS", "AttnError", "lib", "library_path",
+    "attn_fwd", "attn_fwd_chunk", "attn_merge_lse2_host", "attn_status_string", "forward",
+    "merge_lse2_host",
+]
+
+ATTN_BF16 = 0
+ATTN_FP8_E4M3FN = 1
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_HEAD_DIM", 4: "ATTN_ERR_DTYPE",
+    5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_OVERFLOW", 7: "ATTN_ERR_SCALE", 8: "ATTN_ERR_HIP",
+}
+EXPORTED = ("attn_fwd", "attn_fwd_chunk", "attn_merge_lse2_host", "attn_status_string")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libattn.so")
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = int(status)
+        super().__init__(f"{where}: {attn_status_string(status)}" if where else attn_status_string(status))
+
+
+def lib():
+    """Load libattn.so (once). Raises OSError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise OSError(f"{library_path} not built; run `python -m head_attention_amd.build`")
+        L = ctypes.CDLL(library_path)
+        vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+        fwd_args = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32, vp, vp, vp]
+        L.attn_fwd.argtypes = fwd_args + [vp]
+        L.attn_fwd.restype = i32
+        L.attn_fwd_chunk.argtypes = fwd_args + [i64, vp]
+        L.attn_fwd_chunk.restype = i32
+        L.attn_merge_lse2_host.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64]
+        L.attn_merge_lse2_host.restype = i32
+        L.attn_status_string.argtypes = [i32]
+        L.attn_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr() or None
+    if hasattr(x, "ctypes"):  # numpy array (host pointers of the merge)
+        return x.ctypes.data or None
+    raise TypeError(f"cannot take the address of {type(x)!r}")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype,
+             q_descale=None, k_descale=None, v_descale=None, stream=0):
+    return lib().attn_fwd(_addr(q), _addr(k), _addr(v), _addr(out), _addr(lse), B, Hq, Hkv, Sq, Skv, D,
+                          float(scale), int(bool(causal)), int(dtype),
+                          _addr(q_descale), _addr(k_descale), _addr(v_descale), _stream(stream))
+
+
+def attn_fwd_chunk(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype,
+                   q_descale=None, k_descale=None, v_descale=None, kv_start=0, stream=0):
+    return lib().attn_fwd_chunk(_addr(q), _addr(k), _addr(v), _addr(out), _addr(lse), B, Hq, Hkv, Sq, Skv,
+                                D, float(scale), int(bool(causal)), int(dtype),
+                                _addr(q_descale), _addr(k_descale), _addr(v_descale), int(kv_start),
+                                _stream(stream))
+
+
+def attn_merge_lse2_host(o1, lse1, o2, lse2, o_out, lse_out, B, H, S, D):
+    return lib().attn_merge_lse2_host(_addr(o1), _addr(lse1), _addr(o2), _addr(lse2), _addr(o_out),
+                                      _addr(lse_out), B, H, S, D)
+
+
+def attn_status_string(status):
+    return lib().attn_status_string(int(status)).decode()
+
+
+def forward(q, k, v, scale=None, causal=False, q_descale=None, k_descale=None, v_descale=None,
+            kv_start=0, out=None, lse=None, stream=None):
+    """(out, lse) for torch tensors q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] on the GPU.
+
+    q/k/v are torch.bfloat16 or torch.float8_e4m3fn; descales are one-element
+    float32 device tensors or None.
+    """
+    import torch
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if q.dtype == torch.bfloat16:
+        dt = ATTN_BF16
+    elif q.dtype == torch.float8_e4m3fn:
+        dt = ATTN_FP8_E4M3FN
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for t in (q, k, v):
+        if t.dtype != q.dtype or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("q, k, v must be contiguous GPU tensors of one dtype")
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = attn_fwd_chunk(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dt,
+                        q_descale, k_descale, v_descale, kv_start, stream)
+    if st != 0:
+        raise AttnError(st, "attn_fwd_chunk")
+    return out, lse
+
+
+def merge_lse2_host(o1, lse1, o2, lse2):
+    """Merge two host (numpy) partial results: o* uint16 bf16 bits [B,H,S,D], lse* float32 [B,H,S]."""
+    import numpy as np
+    o1 = np.ascontiguousarray(o1, dtype=np.uint16)
+    o2 = np.ascontiguousarray(o2, dtype=np.uint16)
+    l1 = np.ascontiguousarray(lse1, dtype=np.float32)
+    l2 = np.ascontiguousarray(lse2, dtype=np.float32)
+    B, H, S, D = o1.shape
+    if o2.shape != o1.shape or l1.shape != (B, H, S) or l2.shape != (B, H, S):
+        raise ValueError("shape mismatch")
+    oo = np.empty_like(o1)
+    lo = np.empty_like(l1)
+    st = attn_merge_lse2_host(o1, l1, o2, l2, oo, lo, B, H, S, D)
+    if st != 0:
+        raise AttnError(st, "attn_merge_lse2_host")
+    return oo, lo

@@ -1,0 +1,448 @@
+// Fused attention forward with per-row LSE for gfx950 (MI355X, CDNA4).
+//
+// The method is the flash-style attention forward the pages turn on: the SDPA
+// forward with log-sum-exp of the page "[Proposal] ROCm (AMD Instinct) support
+// for the core attention and distributed init" ("Where it breaks on ROCm"),
+// and the bf16 / fp8 (per-tensor q/k/v descale) forward of the page "F8 fmha
+// ASM gfx950" (Test Result section), whose fp8 kernel runs the 32x32x64 fp8
+// MFMA for head dim 128 (Technical Details section). Grouped KV heads follow
+// the 32/8-head layout and the causal prefill of the page "feat(attention):
+// add strict bitwise ROCm path" (ROCm Validation, Benchmark results).
+//
+// Design (gfx950 first; nothing here is translated from another kernel):
+//  * One workgroup = 8 wavefronts = 256 query rows of one (batch, head); each
+//    wave owns 32 rows. The grid covers B * Hq * ceil(Sq / 256) workgroups.
+//  * K and V stream through LDS in tiles of 64 keys, double buffered, with
+//    buffer_load ... lds (global -> LDS without VGPRs). Out-of-range key rows
+//    read as zero through the buffer descriptor's range check.
+//  * Scores are computed transposed, S^T = K Q^T, on 32x32 MFMAs (bf16
+//    32x32x16, or fp8 32x32x64): each lane then owns one query row's scores,
+//    so row max / row sum are in-register work plus one permlane32 swap.
+//  * O^T += V^T P^T keeps P in the registers the score MFMA produced; V^T
+//    operands come from LDS with the transposing reads ds_read_b64_tr_b16
+//    (bf16) and ds_read_b64_tr_b8 (fp8). The key order inside a tile is
+//    permuted consistently between P and V, which leaves the sum unchanged.
+//  * Online softmax in base 2: m = running max of scale*log2(e)*s, p =
+//    exp2(c*s - m), O and l rescaled by exp2(m_old - m_new) only when a row
+//    max grows (a wave-uniform branch).
+//  * fp8: p is formed as 2^8 * p (exponent offset folded into exp2) so that
+//    p in e4m3fn keeps full precision for the typical p ~ 1e-2; l sums the
+//    same scaled fp32 values, and the epilogue divides by l and multiplies by
+//    v_descale, so the 2^8 cancels exactly.
+//  * Causal: a workgroup only loads the key tiles its rows can see; within
+//    them a wave skips tiles entirely above its rows and masks only tiles that
+//    cross its diagonal. Causal grids run the longest query tiles first.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+
+namespace hat {
+
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;   // query rows per workgroup
+constexpr int kBN = 64;            // keys per K/V tile
+constexpr int kRsrcWord3 = 0x00020000;
+
+struct Params {
+  const char* q;
+  const char* k;
+  const char* v;
+  char* o;
+  float* lse;
+  int B, Hq, Hkv, Sq, Skv, group, n_qtiles, kv_start;
+  float c;  // scale * log2(e)
+  const float* qd;
+  const float* kd;
+  const float* vd;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// Exchange a value with the lane 32 away and combine: returns f(x, x^32) on every lane.
+__device__ __forceinline__ float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// LDS layout of one K or V tile: kBN rows of ROWB bytes, 16-byte chunks permuted
+// within a row by an XOR swizzle so that the MFMA operand reads hit distinct banks.
+template <int D, bool FP8>
+struct Tile {
+  static constexpr int ELT = FP8 ? 1 : 2;
+  static constexpr int ROWB = D * ELT;        // bytes per key row
+  static constexpr int CH = ROWB / 16;        // 16-byte chunks per row
+  static constexpr int RP = 256 / ROWB;       // rows per 256 bytes
+  static constexpr int BYTES = kBN * ROWB;
+  static constexpr int NINSTR = BYTES / 1024; // 64-lane x 16-byte loads per tile and matrix
+  // K operand reads: 16 consecutive rows, same logical chunk -> distinct banks.
+  __device__ static __forceinline__ int kswz(int r) { return (r / RP) & (CH - 1); }
+  // V operand reads (transposing): bf16 reads 4 rows x 32 bytes per 16 lanes,
+  // fp8 reads rows {0..3, 8..11} (+4 for the upper half-wave) x 16 bytes.
+  __device__ static __forceinline__ int vswz(int r) {
+    if constexpr (FP8) return (r / RP) & (CH - 1);
+    else return ((r & (CH / 2 - 1)) << 1);
+  }
+};
+
+template <int D, bool CAUSAL, bool FP8>
+__global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
+  using T = Tile<D, FP8>;
+  constexpr int ROWB = T::ROWB;
+  constexpr int NDB = D / 32;                       // 32-wide output column blocks
+  constexpr int NKB = kBN / 32;                     // 32-key blocks per tile
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * T::BYTES];  // [stage][K, V]
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+
+  const int BH = p.B * p.Hq;
+  int bh, qt;
+  if (CAUSAL) {  // longest rows first
+    qt = p.n_qtiles - 1 - (int)(blockIdx.x / BH);
+    bh = (int)(blockIdx.x % BH);
+  } else {
+    bh = (int)(blockIdx.x / p.n_qtiles);
+    qt = (int)(blockIdx.x % p.n_qtiles);
+  }
+  const int b = bh / p.Hq, h = bh % p.Hq, hk = h / p.group;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 5, n = lane & 31;
+  const int q0 = qt * kBM, qw = q0 + wave * 32, qi = qw + n;
+
+  const size_t qrow0 = (size_t)(b * p.Hq + h) * (size_t)p.Sq;
+  const size_t krow0 = (size_t)(b * p.Hkv + hk) * (size_t)p.Skv;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qrow0 * ROWB, (uint32_t)p.Sq * ROWB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + krow0 * ROWB, (uint32_t)p.Skv * ROWB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + krow0 * ROWB, (uint32_t)p.Skv * ROWB);
+
+  float c = p.c, oscale = 1.f;
+  if constexpr (FP8) {
+    const float qd = p.qd ? *p.qd : 1.f, kd = p.kd ? *p.kd : 1.f, vd = p.vd ? *p.vd : 1.f;
+    c *= qd * kd;
+    oscale = vd;
+  }
+
+  // Key tiles this workgroup needs, and those this wave needs.
+  const int rows_end = min(q0 + kBM, p.Sq);
+  const int kv_end = CAUSAL ? min(p.Skv, max(0, rows_end - p.kv_start)) : p.Skv;
+  const int ntiles = (kv_end + kBN - 1) / kBN;
+  const bool wave_live = qw < p.Sq;
+  const int w_kv_end = CAUSAL ? min(p.Skv, max(0, min(qw + 32, p.Sq) - p.kv_start)) : p.Skv;
+  const int w_ntiles = wave_live ? (w_kv_end + kBN - 1) / kBN : 0;
+
+  // Q fragments (B operand of S^T = K Q^T); rows >= Sq read as zero.
+  bf16x8 qf16[FP8 ? 1 : D / 16];
+  i32x8 qf8[FP8 ? D / 64 : 1];
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+      u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, qi * ROWB + (16 * dc + 8 * g) * 2, 0, 0);
+      qf16[dc] = __builtin_bit_cast(bf16x8, x);
+    }
+  } else {
+#pragma unroll
+    for (int dc = 0; dc < D / 64; ++dc) {
+      u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(rq, qi * ROWB + 64 * dc + 32 * g, 0, 0);
+      u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(rq, qi * ROWB + 64 * dc + 32 * g + 16, 0, 0);
+      qf8[dc] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                      (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    }
+  }
+
+  // Clear both stages once, so that tail rows never expose uninitialised LDS.
+  for (int i = threadIdx.x; i < 2 * 2 * T::BYTES / 16; i += kThreads)
+    *(LDS_AS u32x4*)(smem + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  // Global -> LDS for tile t into stage s: wave w issues loads w, w+8, ... of the
+  // 2*NINSTR 1-KB pieces (K first, then V). LDS is written lane-linearly, so the
+  // swizzle is applied to the global address each lane fetches.
+  auto issue = [&](int s, int t) {
+    const int key0 = t * kBN;
+#pragma unroll
+    for (int ins = wave; ins < 2 * T::NINSTR; ins += kWaves) {
+      const bool isv = ins >= T::NINSTR;
+      const int c0 = (isv ? ins - T::NINSTR : ins) * 64;
+      const int cidx = c0 + lane;
+      const int r = cidx / T::CH, pc = cidx % T::CH;
+      const int lc = pc ^ (isv ? T::vswz(r) : T::kswz(r));
+      const int goff = (key0 + r) * ROWB + lc * 16;
+      LDS_AS char* dst = smem + (s * 2 + (isv ? 1 : 0)) * T::BYTES + c0 * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (LDS_AS void*)dst, 16, goff, 0, 0, 0);
+    }
+  };
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  // Per-lane constant parts of the LDS operand addresses.
+  // K operand (A of S^T): row 32*kb + n, logical chunk per dc.
+  const int krow = n;
+  // V operand (A of O^T), transposing reads.
+  const int l16 = lane & 15, dgrp = (lane >> 4) & 1;
+
+  if (ntiles > 0) issue(0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < ntiles) issue((t + 1) & 1, t + 1);
+    if (t >= w_ntiles) continue;
+    const LDS_AS char* ks = smem + ((t & 1) * 2 + 0) * T::BYTES;
+    const LDS_AS char* vs = smem + ((t & 1) * 2 + 1) * T::BYTES;
+
+    // ---- S^T = K Q^T ----
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
+      const int r = 32 * kb + krow;
+      const LDS_AS char* krowp = ks + r * ROWB;
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+          const int lc = 2 * dc + g;
+          const bf16x8 kf = *(const LDS_AS bf16x8*)(krowp + ((lc ^ T::kswz(r)) * 16));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf16[dc], s[kb], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int dc = 0; dc < D / 64; ++dc) {
+          const int lc = 4 * dc + 2 * g;
+          const i32x4 k0 = *(const LDS_AS i32x4*)(krowp + ((lc ^ T::kswz(r)) * 16));
+          const i32x4 k1 = *(const LDS_AS i32x4*)(krowp + (((lc + 1) ^ T::kswz(r)) * 16));
+          const i32x8 kf = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf8[dc], s[kb], 0, 0, 0, 127, 0, 127);
+        }
+      }
+    }
+
+    // ---- mask: keys past Skv, and (causal) keys after the query ----
+    const int key0 = t * kBN;
+    const bool need_mask = (key0 + kBN > p.Skv) || (CAUSAL && key0 + kBN - 1 + p.kv_start > qw);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+          const bool ok = key < p.Skv && (!CAUSAL || key + p.kv_start <= qi);
+          s[kb][i] = ok ? s[kb][i] : -INFINITY;
+        }
+    }
+
+    // ---- online softmax (base 2) ----
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = xor32_max(mx);
+    const float m_new = fmaxf(m, mx * c);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    if (__any(m_new > m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+    }
+    m = m_new;
+    const float moff = (FP8 ? 8.f : 0.f) - m_use;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, moff));
+        s[kb][i] = pv;
+        rs += pv;
+      }
+    l += rs;
+
+    // ---- O^T += V^T P^T ----
+    if constexpr (!FP8) {
+      const int rr = l16 >> 2, ss = l16 & 3;
+#pragma unroll
+      for (int kg = 0; kg < kBN / 16; ++kg) {  // 16-key groups
+        const int kb = kg >> 1, half = kg & 1;
+        bf16x8 pf;
+        {
+          const u32x4 pk = u32x4{pack_bf16(s[kb][8 * half + 0], s[kb][8 * half + 1]),
+                                 pack_bf16(s[kb][8 * half + 2], s[kb][8 * half + 3]),
+                                 pack_bf16(s[kb][8 * half + 4], s[kb][8 * half + 5]),
+                                 pack_bf16(s[kb][8 * half + 6], s[kb][8 * half + 7])};
+          pf = __builtin_bit_cast(bf16x8, pk);
+        }
+        const int key1 = 32 * kb + 16 * half + 4 * g + rr;   // keys key1, key1+8
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int col = 32 * db + 16 * dgrp + 4 * ss;
+          const int lc = col >> 3, hb = (col & 7) * 2;
+          const LDS_AS char* a1 = vs + key1 * ROWB + ((lc ^ T::vswz(key1)) * 16) + hb;
+          const LDS_AS char* a2 = vs + (key1 + 8) * ROWB + ((lc ^ T::vswz(key1 + 8)) * 16) + hb;
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a1);
+          const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a2);
+          const i16x8 vv = i16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[db], 0, 0, 0);
+        }
+      }
+    } else {
+      const int rr = l16 >> 1, hh = l16 & 1;
+#pragma unroll
+      for (int kq = 0; kq < kBN / 64; ++kq) {  // 64-key groups (one fp8 MFMA deep)
+        int pw[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int j = 4 * w, kb = 2 * kq + (j >> 4), i = j & 15;
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i], s[kb][i + 1], 0, false);
+          x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i + 2], s[kb][i + 3], x, true);
+          pw[w] = x;
+        }
+        const i32x8 pf = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int lc = 2 * db + dgrp;
+          int vw[8];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int key = 64 * kq + 32 * (u >> 1) + 16 * (u & 1) + 8 * (rr >> 2) + 4 * g + (rr & 3);
+            const LDS_AS char* a = vs + key * ROWB + ((lc ^ T::vswz(key)) * 16) + 8 * hh;
+            const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)a);
+            vw[2 * u] = x[0];
+            vw[2 * u + 1] = x[1];
+          }
+          const i32x8 vf = i32x8{vw[0], vw[1], vw[2], vw[3], vw[4], vw[5], vw[6], vw[7]};
+          o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, o[db], 0, 0, 0, 127, 0, 127);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: O = O_acc * oscale / l (bf16), LSE = ln2 * (m + log2 l) ----
+  if (!wave_live) return;
+  const float ltot = xor32_sum(l);
+  const float inv = ltot > 0.f ? oscale / ltot : 0.f;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + qrow0 * (size_t)(D * 2), (uint32_t)p.Sq * D * 2);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const u32x2 w = u32x2{pack_bf16(o[db][4 * ii + 0] * inv, o[db][4 * ii + 1] * inv),
+                            pack_bf16(o[db][4 * ii + 2] * inv, o[db][4 * ii + 3] * inv)};
+      const int col = 32 * db + 8 * ii + 4 * g;
+      __builtin_amdgcn_raw_buffer_store_b64(w, ro, (qi * D + col) * 2, 0, 0);
+    }
+  if (g == 0) {
+    const float lse = ltot > 0.f ? (m + __log2f(ltot) - (FP8 ? 8.f : 0.f)) * 0.69314718055994531f : -INFINITY;
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + qrow0, (uint32_t)p.Sq * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
+  }
+}
+
+typedef void (*kernel_fn)(Params);
+
+template <int D, bool FP8>
+kernel_fn pick(bool causal) {
+  return causal ? attn_fwd_kernel<D, true, FP8> : attn_fwd_kernel<D, false, FP8>;
+}
+
+}  // namespace hat
+
+using namespace hat;
+
+static attn_status_t launch(const void* q, const void* k, const void* v, void* out, float* lse,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                            float scale, int causal, attn_dtype_t dtype,
+                            const float* qd, const float* kd, const float* vd, int64_t kv_start,
+                            void* stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3FN) return ATTN_ERR_DTYPE;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || kv_start < 0) return ATTN_ERR_SHAPE;
+  if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return ATTN_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
+  const int64_t elt = dtype == ATTN_BF16 ? 2 : 1;
+  const int64_t rowb = D * elt;
+  const bool any_q = B > 0 && Hq > 0 && Sq > 0;
+  const bool any_kv = B > 0 && Hkv > 0 && Skv > 0;
+  if (!any_q) return ATTN_OK;  // nothing to compute
+  if (!q || !out || !lse) return ATTN_ERR_NULL;
+  if (any_kv && (!k || !v)) return ATTN_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)k | (uintptr_t)v) & 15) return ATTN_ERR_ALIGN;
+  if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
+  // Per-head slices are addressed with 32-bit offsets (plus one tile of slack).
+  const int64_t lim = (int64_t)1 << 31;
+  if ((Sq + kBM) * D * 2 >= lim || (Skv + kBN) * rowb >= lim || Sq + kBM >= lim || kv_start >= lim) return ATTN_ERR_OVERFLOW;
+  const int64_t n_qtiles = (Sq + kBM - 1) / kBM;
+  const int64_t grid = B * Hq * n_qtiles;
+  if (B * Hq >= lim || grid >= lim) return ATTN_ERR_OVERFLOW;
+
+  Params p;
+  p.q = (const char*)q;
+  p.k = (const char*)k;
+  p.v = (const char*)v;
+  p.o = (char*)out;
+  p.lse = lse;
+  p.B = (int)B;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.Sq = (int)Sq;
+  p.Skv = any_kv ? (int)Skv : 0;
+  p.group = (int)(Hq / Hkv);
+  p.n_qtiles = (int)n_qtiles;
+  p.kv_start = (int)kv_start;
+  p.c = scale * 1.4426950408889634f;
+  p.qd = dtype == ATTN_FP8_E4M3FN ? qd : nullptr;
+  p.kd = dtype == ATTN_FP8_E4M3FN ? kd : nullptr;
+  p.vd = dtype == ATTN_FP8_E4M3FN ? vd : nullptr;
+
+  kernel_fn fn;
+  if (dtype == ATTN_BF16) fn = D == 128 ? pick<128, false>(causal) : pick<64, false>(causal);
+  else fn = D == 128 ? pick<128, true>(causal) : pick<64, true>(causal);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                                  float scale, int causal, attn_dtype_t dtype,
+                                  const float* q_descale, const float* k_descale, const float* v_descale,
+                                  void* stream) {
+  return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, q_descale, k_descale,
+                v_descale, 0, stream);
+}
+
+extern "C" attn_status_t attn_fwd_chunk(const void* q, const void* k, const void* v, void* out, float* lse,
+                                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                                        float scale, int causal, attn_dtype_t dtype,
+                                        const float* q_descale, const float* k_descale,
+                                        const float* v_descale, int64_t kv_start, void* stream) {
+  return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, q_descale, k_descale,
+                v_descale, kv_start, stream);
+}

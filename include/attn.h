@@ -1,0 +1,126 @@
+/*
+ * attn.h — C ABI of the MI355X (gfx950) fused attention forward.
+ *
+ * The operation is the fused scaled-dot-product attention forward that also
+ * returns the per-row log-sum-exp, as used through the flash/efficient SDPA
+ * kernels on the page "[Proposal] ROCm (AMD Instinct) support for the core
+ * attention and distributed init" (section "Where it breaks on ROCm" and the
+ * follow-up on compute_log_sumexp) and as the fmha_v3_fwd call on the page
+ * "F8 fmha ASM gfx950" (Test Result section: softmax_scale, is_causal,
+ * return_softmax_lse, out, q/k/v_descale):
+ *
+ *     O[b,h,i,:] = sum_j softmax_j(scale * q_i . k_j  [masked]) * v_j
+ *     LSE[b,h,i] = ln sum_j exp(scale * q_i . k_j)      (allowed j only)
+ *
+ * with query head h reading KV head h / (Hq / Hkv) (grouped KV heads, as in
+ * the 32/8-head layout on the page "feat(attention): add strict bitwise ROCm
+ * path", ROCm Validation section). The (out, lse) pair is what that page's
+ * attention boundary returns, and what a later merge of key chunks needs.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers are DEVICE pointers unless the name or comment says host. The
+ * caller owns every buffer; the library never allocates, frees or
+ * synchronises. Work is enqueued on `stream` (a hipStream_t; NULL = the
+ * default stream) and the call returns at once. Calls are stateless and
+ * re-entrant; identical inputs give bitwise-identical outputs.
+ *
+ * Layouts (all contiguous, row-major):
+ *   q, out : [B, Hq,  Sq,  D]     k, v : [B, Hkv, Skv, D]     lse : [B, Hq, Sq] fp32
+ * Element types: q, k, v are bf16 (ATTN_BF16) or OCP FP8 e4m3fn codes
+ * (ATTN_FP8_E4M3FN); out is always bf16 (round to nearest even); lse is fp32
+ * in natural log and includes the softmax scale.
+ *
+ * Errors: every argument is checked before anything is enqueued; on any
+ * error nothing is launched and an ATTN_ERR_* code is returned. There is no
+ * fallback to another implementation.
+ */
+#ifndef HEAD_ATTENTION_AMD_ATTN_H
+#define HEAD_ATTENTION_AMD_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_BF16 = 0,        /* q, k, v hold bf16 */
+  ATTN_FP8_E4M3FN = 1   /* q, k, v hold e4m3fn codes; real value = decode(code) * descale */
+} attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,      /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,     /* a negative size, Hkv = 0 with Hq > 0, Hq % Hkv != 0, kv_start < 0 */
+  ATTN_ERR_HEAD_DIM = 3,  /* D is not 64 or 128 */
+  ATTN_ERR_DTYPE = 4,     /* unknown attn_dtype_t */
+  ATTN_ERR_ALIGN = 5,     /* q, k, v or out not 16-byte aligned, or lse not 4-byte aligned */
+  ATTN_ERR_OVERFLOW = 6,  /* one head's slice reaches 2^31 bytes, or the grid is too large */
+  ATTN_ERR_SCALE = 7,     /* scale is not finite or not > 0 */
+  ATTN_ERR_HIP = 8        /* the kernel launch failed */
+} attn_status_t;
+
+/*
+ * attn_fwd — O and LSE of the attention forward.
+ *
+ *   q, k, v      device inputs, layouts above, type `dtype`.
+ *   out          device bf16 output [B, Hq, Sq, D].
+ *   lse          device fp32 output [B, Hq, Sq].
+ *   B, Hq, Hkv   batch, query heads, KV heads (Hq % Hkv == 0).
+ *   Sq, Skv      query and key lengths. Zero is allowed: Sq = 0 (or B = 0,
+ *                Hq = 0) enqueues nothing; Skv = 0 writes O = 0, LSE = -inf.
+ *   D            head dimension, 64 or 128.
+ *   scale        softmax scale (finite, > 0), e.g. 1/sqrt(D).
+ *   causal       nonzero: key j is allowed for query i iff j <= i (top-left).
+ *   q/k/v_descale  fp8 only: device pointers to one fp32 each; NULL means 1.
+ *                Ignored for bf16.
+ *   stream       hipStream_t to enqueue on.
+ *
+ * A row with no allowed key gets O = 0 and LSE = -inf.
+ */
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                       float scale, int causal, attn_dtype_t dtype,
+                       const float* q_descale, const float* k_descale, const float* v_descale,
+                       void* stream);
+
+/*
+ * attn_fwd_chunk — attn_fwd over one chunk of keys that starts at absolute
+ * key position kv_start (>= 0): with causal, key j of the chunk is allowed for
+ * query i iff j + kv_start <= i. With kv_start = 0 it equals attn_fwd. The
+ * (out, lse) of several chunks over disjoint key ranges combine with
+ * attn_merge_lse2_host (two chunks) into the attention over their union, the
+ * out/LSE merge the page "feat(attention): add strict bitwise ROCm path"
+ * performs across context-parallel ranks (Summary table, CP communication).
+ */
+attn_status_t attn_fwd_chunk(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                             float scale, int causal, attn_dtype_t dtype,
+                             const float* q_descale, const float* k_descale, const float* v_descale,
+                             int64_t kv_start, void* stream);
+
+/*
+ * attn_merge_lse2_host — merge two partial results on the HOST.
+ *
+ *   o1, o2, o_out  host bf16 bit patterns [B, H, S, D]
+ *   lse1, lse2, lse_out  host fp32 [B, H, S] (natural log)
+ *
+ * For each row: L = ln(e^L1 + e^L2), O = e^(L1-L) O1 + e^(L2-L) O2, computed
+ * in fp32 and rounded to bf16 (nearest even). Both L1 and L2 = -inf gives
+ * O = 0, L = -inf. Output buffers may alias the inputs element for element.
+ * Returns ATTN_ERR_NULL / ATTN_ERR_SHAPE on bad arguments; runs synchronously.
+ */
+attn_status_t attn_merge_lse2_host(const uint16_t* o1, const float* lse1,
+                                   const uint16_t* o2, const float* lse2,
+                                   uint16_t* o_out, float* lse_out,
+                                   int64_t B, int64_t H, int64_t S, int64_t D);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* attn_status_string(attn_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HEAD_ATTENTION_AMD_ATTN_H */

@@ -1,0 +1,119 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol,
+refuses bad arguments before touching a device, and its host-side merge
+matches the oracle's merge. No kernel is launched here."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import head_attention_amd as ha
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ha.library_path):
+        from head_attention_amd.build import build
+        build()
+    return ha.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(ha.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), f"missing export {n}"
+
+
+def test_status_strings(L):
+    for code, name in ha.STATUS.items():
+        assert ha.attn_status_string(code).startswith(name)
+    assert ha.attn_status_string(99) == "ATTN_ERR_UNKNOWN"
+
+
+# A fake, 16-byte aligned, never-dereferenced address: validation returns before any use.
+P = 1 << 20
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(D=96), 3),
+    (dict(D=0), 3),
+    (dict(dtype=2), 4),
+    (dict(Hq=3, Hkv=2), 2),
+    (dict(Hkv=0), 2),
+    (dict(Sq=-1), 2),
+    (dict(B=-2), 2),
+    (dict(kv_start=-1), 2),
+    (dict(scale=float("nan")), 7),
+    (dict(scale=float("inf")), 7),
+    (dict(scale=0.0), 7),
+    (dict(scale=-1.0), 7),
+    (dict(q=None), 1),
+    (dict(out=None), 1),
+    (dict(lse=None), 1),
+    (dict(k=None), 1),
+    (dict(q=P + 8), 5),
+    (dict(v=P + 4), 5),
+    (dict(lse=P + 2), 5),
+    (dict(Sq=1 << 30), 6),
+    (dict(Skv=1 << 30), 6),
+])
+def test_fail_closed_validation(L, args, status):
+    a = dict(q=P, k=P, v=P, out=P, lse=P, B=1, Hq=4, Hkv=2, Sq=100, Skv=100, D=128, scale=0.1,
+             causal=0, dtype=0, kv_start=0)
+    a.update(args)
+    st = ha.attn_fwd_chunk(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
+                           a["Skv"], a["D"], a["scale"], a["causal"], a["dtype"], None, None, None,
+                           a["kv_start"], 0)
+    assert st == status, (args, ha.STATUS.get(st, st))
+
+
+def test_zero_queries_return_ok_without_launch(L):
+    assert ha.attn_fwd(None, None, None, None, None, 1, 4, 2, 0, 100, 128, 0.1, 0, 0) == 0
+    assert ha.attn_fwd(None, None, None, None, None, 0, 4, 2, 10, 100, 128, 0.1, 0, 0) == 0
+
+
+def _bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _unbits(b):
+    return torch.from_numpy(np.asarray(b).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def test_host_merge_matches_oracle_merge(L):
+    r = np.random.default_rng(0)
+    B, H, S, D = 2, 3, 50, 64
+    o1, o2 = r.standard_normal((B, H, S, D)), r.standard_normal((B, H, S, D))
+    l1, l2 = r.standard_normal((B, H, S)) * 3, r.standard_normal((B, H, S)) * 3
+    l1[0, 0, :5] = -np.inf
+    l2[0, 0, 3:8] = -np.inf
+    b1, b2 = _bits(o1), _bits(o2)
+    f1, f2 = np.float32(l1), np.float32(l2)
+    om, lm = ha.merge_lse2_host(b1, f1, b2, f2)
+    Oref, Lref = oracle.merge_lse([(_unbits(b1), f1.astype(np.float64)), (_unbits(b2), f2.astype(np.float64))])
+    got = _unbits(om)
+    assert np.array_equal(np.isneginf(lm), np.isneginf(Lref))
+    assert (got[np.isneginf(Lref)] == 0).all()
+    # one bf16 rounding (half an ulp: 2^-8 relative) plus fp32 arithmetic
+    assert (np.abs(got - Oref) <= 2 ** -8 * np.abs(Oref) * 1.01 + 1e-6).all()
+    fin = np.isfinite(Lref)
+    assert np.abs(lm[fin] - Lref[fin]).max() <= 1e-5
+
+
+def test_host_merge_rejects_bad_arguments(L):
+    assert ha.attn_merge_lse2_host(None, None, None, None, None, None, 1, 1, 1, 4) == 1
+    assert ha.attn_merge_lse2_host(None, None, None, None, None, None, -1, 1, 1, 4) == 2
+    assert ha.attn_merge_lse2_host(None, None, None, None, None, None, 0, 1, 1, 4) == 0
