@@ -1,6 +1,7 @@
 """Benchmark of the gfx950 attention forward at the video-DiT shape.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --copy-calibration MIB   # plain device copy of known size, for HBM counters
 
 One step is the whole hot path over one batch: the bf16 forward at
 B1 H5 S75600 D128 (non-causal) and the fp8 (e4m3fn, per-tensor descale)
@@ -50,6 +51,25 @@ def algorithmic_bytes(B, Hq, Hkv, Sq, Skv, D, elt):
     return (B * Hq * Sq * D + 2 * B * Hkv * Skv * D) * elt + B * Hq * Sq * D * 2 + B * Hq * Sq * 4
 
 
+def measured_traffic():
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter summary.
+
+    Returns {dtype: bytes} while the kernel source still hashes to what the
+    counters were taken on, else {} (the figure is then reported as null).
+    """
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "attn_fwd_kernel_video_dit_B1H5S75600D128_hbm_traffic.md")
+    src = os.path.join(ROOT, "head_attention_amd", "csrc", "attn_fwd.hip")
+    try:
+        line = [l for l in open(prof) if l.startswith("traffic_json: ")][0]
+        rec = json.loads(line[len("traffic_json: "):])
+        if rec["source_sha256"] != hashlib.sha256(open(src, "rb").read()).hexdigest():
+            return {}
+        return rec["bytes_per_launch"]
+    except (OSError, IndexError, KeyError, ValueError):
+        return {}
+
+
 def cpu_baseline(inp, w, budget_s):
     """Time the fp64 oracle on a bounded sample of query rows of the same workload."""
     import numpy as np
@@ -90,6 +110,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device-to-device copies of MIB MiB each (scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no sharding or collectives); use --gpus 1",
@@ -98,6 +121,15 @@ def main():
 
     import numpy as np
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
     import head_attention_amd as ha
     from synth import WORKLOADS, make_inputs
 
@@ -159,9 +191,11 @@ def main():
     value = 2 * flops / (wall / args.steps) / 1e12
     base_combined = 2 * flops / ((PAGES_US["bf16"] + PAGES_US["fp8"]) * 1e-6) / 1e12
 
+    traffic = measured_traffic()
+
     def roof(tf, dt, t, elt):
         return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
-                "frac": round(tf / PEAK_TFLOPS[dt], 4), "traffic": None,
+                "frac": round(tf / PEAK_TFLOPS[dt], 4), "traffic": traffic.get(dt),
                 "kernel": f"attn_fwd_kernel<128,false,{'true' if dt == 'fp8' else 'false'}>",
                 "mean_launch_ms": round(t * 1e3, 4),
                 "algorithmic_bytes": algorithmic_bytes(B, H, H, S, S, D, elt)}
