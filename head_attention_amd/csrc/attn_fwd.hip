@@ -12,9 +12,11 @@
 // Design (gfx950 first; nothing here is translated from another kernel):
 //  * One workgroup = 8 wavefronts = 256 query rows of one (batch, head); each
 //    wave owns 32 rows. The grid covers B * Hq * ceil(Sq / 256) workgroups.
-//  * K and V stream through LDS in tiles of 64 keys, double buffered, with
-//    buffer_load ... lds (global -> LDS without VGPRs). Out-of-range key rows
-//    read as zero through the buffer descriptor's range check.
+//  * K and V stream through LDS in tiles of 64 keys, in a ring of kStages
+//    slots filled kStages-1 tiles ahead by buffer_load ... lds (global -> LDS
+//    without VGPRs); one workgroup barrier per tile publishes a tile and
+//    retires the oldest slot. Out-of-range key rows read as zero through the
+//    buffer descriptor's range check.
 //  * Scores are computed transposed, S^T = K Q^T, on 32x32 MFMAs (bf16
 //    32x32x16, or fp8 32x32x64): each lane then owns one query row's scores,
 //    so row max / row sum are in-register work plus one permlane32 swap.
@@ -22,13 +24,15 @@
 //    operands come from LDS with the transposing reads ds_read_b64_tr_b16
 //    (bf16) and ds_read_b64_tr_b8 (fp8). The key order inside a tile is
 //    permuted consistently between P and V, which leaves the sum unchanged.
-//  * Online softmax in base 2: m = running max of scale*log2(e)*s, p =
-//    exp2(c*s - m), O and l rescaled by exp2(m_old - m_new) only when a row
-//    max grows (a wave-uniform branch).
-//  * fp8: p is formed as 2^8 * p (exponent offset folded into exp2) so that
-//    p in e4m3fn keeps full precision for the typical p ~ 1e-2; l sums the
-//    same scaled fp32 values, and the epilogue divides by l and multiplies by
-//    v_descale, so the 2^8 cancels exactly.
+//  * Online softmax in base 2 with a lazy running max: m tracks the row max
+//    of scale*log2(e)*s but moves only when a tile's row max exceeds it by
+//    more than kTau (8 for bf16, 4 for fp8); then O and l are rescaled by
+//    exp2(m_old - m_new) (a wave-uniform branch, rarely taken). p =
+//    exp2(c*s - m) is thus at most 2^kTau, well inside bf16 and fp32 range.
+//  * fp8: p is formed as 2^(8-kTau) * p (exponent offset folded into exp2),
+//    so p in e4m3fn stays at most 256 and keeps full precision for the
+//    typical p ~ 1e-2; l sums the same scaled, unrounded fp32 values, and the
+//    epilogue divides by l and multiplies by v_descale, so the offset cancels.
 //  * Causal: a workgroup only loads the key tiles its rows can see; within
 //    them a wave skips tiles entirely above its rows and masks only tiles that
 //    cross its diagonal. Causal grids run the longest query tiles first.
@@ -59,6 +63,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;   // query rows per workgroup
 constexpr int kBN = 64;            // keys per K/V tile
 constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kStages = 4;         // LDS ring depth (K/V tiles in flight)
 
 struct Params {
   const char* q;
@@ -75,6 +80,26 @@ struct Params {
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xFFFFu), (int)bytes, kRsrcWord3};
+}
+
+// Direct global->LDS copy of 16 bytes per lane: lane l writes LDS bytes
+// [lds_base + 16 l, +16) from buffer offset voff (out-of-range offsets read as
+// zero). Written as asm so that the compiler does not make later LDS reads of
+// other ring slots wait for it; the kernel waits on vmcnt itself before the
+// barrier that publishes a slot.
+__device__ __forceinline__ void dma16(const i32x4 rsrc, int voff, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds_base) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
 // Exchange a value with the lane 32 away and combine: returns f(x, x^32) on every lane.
@@ -107,8 +132,13 @@ struct Tile {
   // V operand reads (transposing): bf16 reads 4 rows x 32 bytes per 16 lanes,
   // fp8 reads rows {0..3, 8..11} (+4 for the upper half-wave) x 16 bytes.
   __device__ static __forceinline__ int vswz(int r) {
-    if constexpr (FP8) return (r / RP) & (CH - 1);
-    else return ((r & (CH / 2 - 1)) << 1);
+    if constexpr (!FP8) {
+      if constexpr (D == 128) return (r & 3) << 2;
+      else return ((r >> 1) & 1) << 2;
+    } else {
+      if constexpr (D == 128) return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2);
+      else return ((r >> 3) & 1) << 1;
+    }
   }
 };
 
@@ -118,7 +148,9 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   constexpr int ROWB = T::ROWB;
   constexpr int NDB = D / 32;                       // 32-wide output column blocks
   constexpr int NKB = kBN / 32;                     // 32-key blocks per tile
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * T::BYTES];  // [stage][K, V]
+  constexpr float kTau = FP8 ? 4.f : 8.f;           // lazy-max threshold (log2 units)
+  constexpr float kPre = FP8 ? 8.f - kTau : 0.f;    // fp8: p carries a factor 2^kPre
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * 2 * T::BYTES];  // [slot][K, V]
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
 
   const int BH = p.B * p.Hq;
@@ -138,8 +170,9 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   const size_t qrow0 = (size_t)(b * p.Hq + h) * (size_t)p.Sq;
   const size_t krow0 = (size_t)(b * p.Hkv + hk) * (size_t)p.Skv;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qrow0 * ROWB, (uint32_t)p.Sq * ROWB);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + krow0 * ROWB, (uint32_t)p.Skv * ROWB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + krow0 * ROWB, (uint32_t)p.Skv * ROWB);
+  const i32x4 rk = rsrc_words(p.k + krow0 * ROWB, (uint32_t)p.Skv * ROWB);
+  const i32x4 rv = rsrc_words(p.v + krow0 * ROWB, (uint32_t)p.Skv * ROWB);
+  const unsigned smem_addr = (unsigned)(uintptr_t)smem;
 
   float c = p.c, oscale = 1.f;
   if constexpr (FP8) {
@@ -175,26 +208,38 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
     }
   }
 
-  // Clear both stages once, so that tail rows never expose uninitialised LDS.
-  for (int i = threadIdx.x; i < 2 * 2 * T::BYTES / 16; i += kThreads)
+  // Q has landed before any copy is queued behind it: the compiler's own
+  // memory-counter waits for Q then never wait for the copies.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+  // Clear the ring once, so that tail rows never expose uninitialised LDS.
+  for (int i = threadIdx.x; i < kStages * 2 * T::BYTES / 16; i += kThreads)
     *(LDS_AS u32x4*)(smem + i * 16) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
-  // Global -> LDS for tile t into stage s: wave w issues loads w, w+8, ... of the
-  // 2*NINSTR 1-KB pieces (K first, then V). LDS is written lane-linearly, so the
-  // swizzle is applied to the global address each lane fetches.
-  auto issue = [&](int s, int t) {
+  // Global -> LDS for tile t into slot t % kStages: the 2*NINSTR 1-KB pieces
+  // (K first, then V) are split evenly, piece w*PW .. w*PW+PW-1 to wave w. LDS
+  // is written lane-linearly, so the swizzle is applied to the global address
+  // each lane fetches.
+  constexpr int PW = 2 * T::NINSTR / kWaves;   // pieces per wave per tile
+  static_assert(PW >= 1 && PW * kWaves == 2 * T::NINSTR, "tile pieces must split evenly over waves");
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](int t) {
     const int key0 = t * kBN;
+    const int slot = t % kStages;
 #pragma unroll
-    for (int ins = wave; ins < 2 * T::NINSTR; ins += kWaves) {
+    for (int j = 0; j < PW; ++j) {
+      const int ins = wv * PW + j;
       const bool isv = ins >= T::NINSTR;
       const int c0 = (isv ? ins - T::NINSTR : ins) * 64;
       const int cidx = c0 + lane;
       const int r = cidx / T::CH, pc = cidx % T::CH;
       const int lc = pc ^ (isv ? T::vswz(r) : T::kswz(r));
       const int goff = (key0 + r) * ROWB + lc * 16;
-      LDS_AS char* dst = smem + (s * 2 + (isv ? 1 : 0)) * T::BYTES + c0 * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (LDS_AS void*)dst, 16, goff, 0, 0, 0);
+      const unsigned dst = __builtin_amdgcn_readfirstlane(smem_addr + (slot * 2 + (isv ? 1 : 0)) * T::BYTES + c0 * 16);
+      const i32x4 rs = isv ? rv : rk;
+      dma16(i32x4{__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
+                  __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])}, goff, dst);
     }
   };
 
@@ -209,14 +254,22 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   // V operand (A of O^T), transposing reads.
   const int l16 = lane & 15, dgrp = (lane >> 4) & 1;
 
-  if (ntiles > 0) issue(0, 0);
+  // Tiles 0 .. kStages-2 in flight before the loop; iteration t waits for its
+  // own copies of tile t (the copies of later tiles may still be in flight),
+  // then the barrier publishes tile t and retires slot (t-1) % kStages, which
+  // is refilled with tile t + kStages - 1.
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u)
+    if (u < ntiles) issue(u);
   for (int t = 0; t < ntiles; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (t + 2 < ntiles) wait_vmcnt<2 * PW>();
+    else if (t + 1 < ntiles) wait_vmcnt<PW>();
+    else wait_vmcnt<0>();
     __syncthreads();
-    if (t + 1 < ntiles) issue((t + 1) & 1, t + 1);
+    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
     if (t >= w_ntiles) continue;
-    const LDS_AS char* ks = smem + ((t & 1) * 2 + 0) * T::BYTES;
-    const LDS_AS char* vs = smem + ((t & 1) * 2 + 1) * T::BYTES;
+    const LDS_AS char* ks = smem + ((t % kStages) * 2 + 0) * T::BYTES;
+    const LDS_AS char* vs = smem + ((t % kStages) * 2 + 1) * T::BYTES;
 
     // ---- S^T = K Q^T ----
     f32x16 s[NKB];
@@ -259,22 +312,23 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
     }
 
     // ---- online softmax (base 2) ----
+    // Lazy running max: m moves only when a row max passes it by more than
+    // kTau, so p stays below 2^kTau and O is rarely rescaled.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = xor32_max(mx);
-    const float m_new = fmaxf(m, mx * c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    if (__any(m_new > m)) {
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    mx = xor32_max(mx) * c;
+    const bool grow = mx > m + kTau;
+    if (__any(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mx) : 1.f;   // 0 when m was -inf
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      m = grow ? mx : m;
     }
-    m = m_new;
-    const float moff = (FP8 ? 8.f : 0.f) - m_use;
+    const float moff = kPre - (m == -INFINITY ? 0.f : m);
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -360,7 +414,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
       __builtin_amdgcn_raw_buffer_store_b64(w, ro, (qi * D + col) * 2, 0, 0);
     }
   if (g == 0) {
-    const float lse = ltot > 0.f ? (m + __log2f(ltot) - (FP8 ? 8.f : 0.f)) * 0.69314718055994531f : -INFINITY;
+    const float lse = ltot > 0.f ? (m + __log2f(ltot) - kPre) * 0.69314718055994531f : -INFINITY;
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + qrow0, (uint32_t)p.Sq * 4);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
   }

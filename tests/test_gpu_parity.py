@@ -162,9 +162,18 @@ def test_empty_queries_is_a_no_op():
 
 
 def test_large_scores_stay_finite():
-    """Scores of magnitude ~100 (keys scaled by 30): the running max keeps exp2 in range."""
+    """Scores of magnitude ~100 (keys scaled by 30): the running max keeps exp2 in range.
+
+    Outside the N(0,1) regime one key can carry almost all the weight. The
+    kernel only moves its running max when a row max grows by more than 2^8, so
+    the dominant p is a bf16-rounded value in [1, 256] rather than exactly 1:
+    its relative rounding error (2^-8 at most) passes straight into O, hence
+    the bound 1e-2 + 2^-8 * max|V| here instead of 1e-2.
+    """
     say("case large scores")
     inp = synth_inputs(1, 2, 2, 300, 500, 128, "bf16", seed=99, scale_k=30.0)
     O, L, _ = run_gpu(inp, 1 / math.sqrt(128), False)
     Oref, Lref = oracle_ref(inp, 1 / math.sqrt(128), False)
-    check_bf16(O, L, Oref, Lref, lse_tol=2e-3, what="large scores")
+    import oracle
+    vmax = float(np.abs(oracle.dequantise(inp["v"], "bf16")).max())
+    check_bf16(O, L, Oref, Lref, o_tol=1e-2 + 2 ** -8 * vmax, lse_tol=2e-3, what="large scores")
