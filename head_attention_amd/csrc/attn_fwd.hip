@@ -24,15 +24,17 @@
 //    operands come from LDS with the transposing reads ds_read_b64_tr_b16
 //    (bf16) and ds_read_b64_tr_b8 (fp8). The key order inside a tile is
 //    permuted consistently between P and V, which leaves the sum unchanged.
-//  * Online softmax in base 2 with a lazy running max: m tracks the row max
-//    of scale*log2(e)*s but moves only when a tile's row max exceeds it by
-//    more than kTau (8 for bf16, 4 for fp8); then O and l are rescaled by
-//    exp2(m_old - m_new) (a wave-uniform branch, rarely taken). p =
-//    exp2(c*s - m) is thus at most 2^kTau, well inside bf16 and fp32 range.
-//  * fp8: p is formed as 2^(8-kTau) * p (exponent offset folded into exp2),
-//    so p in e4m3fn stays at most 256 and keeps full precision for the
-//    typical p ~ 1e-2; l sums the same scaled, unrounded fp32 values, and the
-//    epilogue divides by l and multiplies by v_descale, so the offset cancels.
+//  * Online softmax in base 2 with a checked running max m (of
+//    scale*log2(e)*s): p = exp2(c*s - m) is formed with the current m, and
+//    as long as every p of a tile stays at most 2^8 (a lane's partial row
+//    sum bounds its own p) the tile needs no row max at all. Otherwise, and
+//    for a row's first tile, m becomes the exact running max, O and l are
+//    rescaled by exp2(m_old - m_new) and p is formed again (a wave-uniform
+//    branch, rarely taken). p <= 2^8 is well inside bf16 and fp32 range.
+//  * fp8: p carries a factor 2^kPre (folded into the exp2 offset), so that
+//    e4m3fn P is at most 2^8 and keeps full precision for the typical
+//    p ~ 1e-2; l sums the same scaled, unrounded fp32 values, and the
+//    epilogue divides by l and multiplies by v_descale, so the factor cancels.
 //  * Causal: a workgroup only loads the key tiles its rows can see; within
 //    them a wave skips tiles entirely above its rows and masks only tiles that
 //    cross its diagonal. Causal grids run the longest query tiles first.
@@ -148,8 +150,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   constexpr int ROWB = T::ROWB;
   constexpr int NDB = D / 32;                       // 32-wide output column blocks
   constexpr int NKB = kBN / 32;                     // 32-key blocks per tile
-  constexpr float kTau = FP8 ? 4.f : 8.f;           // lazy-max threshold (log2 units)
-  constexpr float kPre = FP8 ? 8.f - kTau : 0.f;    // fp8: p carries a factor 2^kPre
+  constexpr float kPre = FP8 ? 4.f : 0.f;           // fp8: p carries a factor 2^kPre
   __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * 2 * T::BYTES];  // [slot][K, V]
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
 
@@ -311,24 +312,15 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
         }
     }
 
-    // ---- online softmax (base 2) ----
-    // Lazy running max: m moves only when a row max passes it by more than
-    // kTau, so p stays below 2^kTau and O is rarely rescaled.
-    float mx = -INFINITY;
+    // ---- online softmax (base 2) with a checked running max. p = exp2(c s - m)
+    // is formed with the current m; while every p of the tile stays at most
+    // 2^8 (a lane's partial row sum bounds its p) m is good enough and no row
+    // max is needed. Otherwise (or while m is still -inf) m becomes the exact
+    // running max, O and l are rescaled, and p is formed again.
+    f32x16 sraw[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = xor32_max(mx) * c;
-    const bool grow = mx > m + kTau;
-    if (__any(grow)) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mx) : 1.f;   // 0 when m was -inf
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      m = grow ? mx : m;
-    }
-    const float moff = kPre - (m == -INFINITY ? 0.f : m);
+    for (int kb = 0; kb < NKB; ++kb) sraw[kb] = s[kb];
+    float moff = kPre - (m == -INFINITY ? 0.f : m);
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -338,6 +330,29 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
         s[kb][i] = pv;
         rs += pv;
       }
+    if (__any(m == -INFINITY || !(rs <= 256.f))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sraw[kb][i]);
+      const float mnew = fmaxf(m, xor32_max(mx) * c);
+      const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 when m was -inf
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      m = mnew;
+      moff = kPre - (m == -INFINITY ? 0.f : m);
+      rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sraw[kb][i], c, moff));
+          s[kb][i] = pv;
+          rs += pv;
+        }
+    }
     l += rs;
 
     // ---- O^T += V^T P^T ----

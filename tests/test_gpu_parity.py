@@ -165,8 +165,9 @@ def test_large_scores_stay_finite():
     """Scores of magnitude ~100 (keys scaled by 30): the running max keeps exp2 in range.
 
     Outside the N(0,1) regime one key can carry almost all the weight. The
-    kernel only moves its running max when a row max grows by more than 2^8, so
-    the dominant p is a bf16-rounded value in [1, 256] rather than exactly 1:
+    kernel keeps its running max while every p = 2^(c s - m) of a tile stays
+    at most 2^8, so the dominant p is a bf16-rounded value in [1, 256] rather
+    than exactly 1:
     its relative rounding error (2^-8 at most) passes straight into O, hence
     the bound 1e-2 + 2^-8 * max|V| here instead of 1e-2.
     """
