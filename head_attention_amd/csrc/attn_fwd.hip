@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -182,6 +183,8 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
     oscale = vd;
   }
 
+  const int Skv = p.Skv, kv_start = p.kv_start;   // read by the tile lambda (no argument struct capture)
+
   // Key tiles this workgroup needs, and those this wave needs.
   const int rows_end = min(q0 + kBM, p.Sq);
   const int kv_end = CAUSAL ? min(p.Skv, max(0, rows_end - p.kv_start)) : p.Skv;
@@ -262,13 +265,16 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
 #pragma unroll
   for (int u = 0; u < kStages - 1; ++u)
     if (u < ntiles) issue(u);
-  for (int t = 0; t < ntiles; ++t) {
+  // One iteration per key tile. Tiles from first_masked on take the element
+  // mask (keys past Skv, or causal keys after the wave's first row); the
+  // others are compiled without it, so no mask work is ever speculated.
+  auto step = [&](int t, auto masked_c) __attribute__((always_inline)) {
     if (t + 2 < ntiles) wait_vmcnt<2 * PW>();
     else if (t + 1 < ntiles) wait_vmcnt<PW>();
     else wait_vmcnt<0>();
     __syncthreads();
     if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
-    if (t >= w_ntiles) continue;
+    if (t >= w_ntiles) return;
     const LDS_AS char* ks = smem + ((t % kStages) * 2 + 0) * T::BYTES;
     const LDS_AS char* vs = smem + ((t % kStages) * 2 + 1) * T::BYTES;
 
@@ -299,15 +305,14 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
     }
 
     // ---- mask: keys past Skv, and (causal) keys after the query ----
-    const int key0 = t * kBN;
-    const bool need_mask = (key0 + kBN > p.Skv) || (CAUSAL && key0 + kBN - 1 + p.kv_start > qw);
-    if (need_mask) {
+    if constexpr (decltype(masked_c)::value) {
+      const int key0 = t * kBN;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-          const bool ok = key < p.Skv && (!CAUSAL || key + p.kv_start <= qi);
+          const bool ok = key < Skv && (!CAUSAL || key + kv_start <= qi);
           s[kb][i] = ok ? s[kb][i] : -INFINITY;
         }
     }
@@ -412,7 +417,12 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
         }
       }
     }
-  }
+  };
+  const int first_masked = CAUSAL ? min(Skv / kBN, max(0, qw - kv_start + 1) / kBN) : Skv / kBN;
+  int t = 0;
+  for (; t < min(first_masked, ntiles); ++t) step(t, std::false_type{});
+  for (; t < ntiles; ++t) step(t, std::true_type{});
+
 
   // ---- epilogue: O = O_acc * oscale / l (bf16), LSE = ln2 * (m + log2 l) ----
   if (!wave_live) return;
