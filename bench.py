@@ -103,6 +103,62 @@ def cpu_baseline(inp, w, budget_s):
                       f"(fp64 numpy oracle, {t:.1f} s; rows are independent, so the rate scales)"}
 
 
+def bench_workload(args, w, make_inputs):
+    """Time one launch configuration of another workload; prints one JSON line."""
+    import numpy as np
+    import torch
+    import head_attention_amd as ha
+    dev = torch.device("cuda:0")
+    fmt = "bf16" if w.fmt in ("f32", "bf16") else w.fmt
+    inp = make_inputs(w, fmt)
+    causal = bool(w.causal[-1])
+
+    def put(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.int16).view(torch.bfloat16) if fmt == "bf16" else t.view(torch.float8_e4m3fn)).to(dev)
+
+    Q, K, V = (put(inp[n]) for n in "qkv")
+    ds = [None] * 3
+    if fmt == "e4m3fn":
+        ds = [torch.tensor([inp[n]], dtype=torch.float32, device=dev) for n in ("q_descale", "k_descale", "v_descale")]
+    O = torch.empty((w.B, w.Hq, w.Sq, w.D), dtype=torch.bfloat16, device=dev)
+    L = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    dt = ha.ATTN_BF16 if fmt == "bf16" else ha.ATTN_FP8_E4M3FN
+
+    def launch():
+        st = ha.attn_fwd(Q, K, V, O, L, w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.scale, int(causal), dt,
+                         ds[0], ds[1], ds[2], stream.cuda_stream)
+        if st != 0:
+            raise ha.AttnError(st, "attn_fwd")
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        launch()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tl = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+    flops = attn_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, causal)
+    tf = flops / tl.mean() / 1e12
+    dtn = "bf16" if fmt == "bf16" else "fp8"
+    print(json.dumps({
+        "metric": f"attn fwd TFLOPS ({dtn}) at {w.name}", "value": round(tf, 2), "unit": "TFLOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtn, "data": "synthetic",
+        "config": {"workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Skv{w.Skv} D{w.D} "
+                               f"{'causal' if causal else 'non-causal'}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "causal": causal},
+        "ms_mean": round(float(tl.mean()) * 1e3, 4), "ms_p50": round(float(np.median(tl)) * 1e3, 4),
+        "frac_of_peak": round(tf / PEAK_TFLOPS[dtn], 4),
+        "workgroups": w.B * w.Hq * ((w.Sq + 255) // 256)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +169,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB each (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
+    ap.add_argument("--workload", default=None,
+                    help="time one other workload of synth.WORKLOADS instead (a context line, not the "
+                         "headline); causal workloads run causal")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no sharding or collectives); use --gpus 1",
@@ -132,6 +191,9 @@ def main():
         return
     import head_attention_amd as ha
     from synth import WORKLOADS, make_inputs
+
+    if args.workload:
+        return bench_workload(args, WORKLOADS[args.workload], make_inputs)
 
     dev = torch.device("cuda:0")
     ha.lib()

@@ -16,7 +16,11 @@ identical numbers. Storage formats:
 The shapes are the five workloads of the attention forward: a tiny fp32 case,
 an LLM-style case, the video-DiT self-attention (bf16 and fp8) and a GQA causal
 case that is also run as two key chunks. The video-DiT shape is the one the
-page "F8 fmha ASM gfx950" benchmarks (b 1, n 5, q 75600, d 128).
+page "F8 fmha ASM gfx950" benchmarks (b 1, n 5, q 75600, d 128). Three more
+have Sq != Skv: the window-30 shape of the page "[Proposal] ROCm (AMD
+Instinct) support for the core attention and distributed init" (query 4680 x
+key 51480, 12 heads), and the cross-attention of the page "F8 fmha ASM gfx950"
+(90000 queries against 512 keys, 40 heads; an even head count), bf16 and fp8.
 """
 
 from dataclasses import dataclass, field
@@ -60,6 +64,13 @@ WORKLOADS = {
         Workload(3, "video_dit", 1, 5, 5, 75600, 75600, 128, "bf16", (False,)),
         Workload(4, "video_dit_fp8", 1, 5, 5, 75600, 75600, 128, "e4m3fn", (False,)),
         Workload(5, "gqa_causal", 1, 32, 8, 8192, 8192, 128, "bf16", (True,), chunks=(4096, 4096)),
+        # Sq != Skv shapes beyond the five above
+        Workload(6, "window30", 1, 12, 12, 4680, 51480, 128, "bf16", (False,),
+                 note="raw SDPA at the window-30 shape, query 4680 x key 51480"),
+        Workload(7, "wan_cross", 1, 40, 40, 90000, 512, 128, "bf16", (False,),
+                 note="cross-attention, 90000 queries against 512 keys, 40 heads"),
+        Workload(8, "wan_cross_fp8", 1, 40, 40, 90000, 512, 128, "e4m3fn", (False,),
+                 note="the same cross-attention in fp8 e4m3fn with per-tensor descales"),
     ]
 }
 

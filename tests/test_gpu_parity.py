@@ -108,6 +108,18 @@ def test_gqa_causal_full_and_chunked_merge():
     check_bf16(Om[:, :, rows], Lm[:, :, rows], Oref, Lref, what="merged vs oracle")
 
 
+@pytest.mark.parametrize("name", ["window30", "wan_cross", "wan_cross_fp8"])
+def test_sq_ne_skv_full_size_sampled_rows(name):
+    """Sq != Skv at full size: query 4680 x key 51480 (12 heads) and 90000 x 512 (40 heads)."""
+    w = WORKLOADS[name]
+    say(f"case {name} full size, sampled rows")
+    inp = make_inputs(w)
+    O, L, _ = run_gpu(inp, w.scale, False)
+    rows = sample_rows(w.Sq, 40, 11)
+    Oref, Lref = oracle_ref(inp, w.scale, False, rows=rows)
+    check(inp, O[:, :, rows], L[:, :, rows], Oref, Lref, what=f"{name} rows={len(rows)}")
+
+
 # ---------------------------------------------------------------- ragged, degenerate, mixed shapes
 
 EDGE = [
@@ -123,6 +135,8 @@ EDGE = [
     (1, 6, 2, 257, 129, 128, False, 0),
     (1, 5, 5, 1000, 2000, 128, False, 0),   # odd head count
     (1, 4, 4, 1000, 512, 128, False, 0),    # even head count, short keys (cross-attention-like)
+    (1, 40, 40, 1500, 512, 128, False, 0),  # the cross-attention head count, even
+    (1, 9, 9, 1500, 512, 128, False, 0),    # and an odd one
 ]
 
 
