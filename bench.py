@@ -125,10 +125,19 @@ def bench_workload(args, w, make_inputs):
     L = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     dt = ha.ATTN_BF16 if fmt == "bf16" else ha.ATTN_FP8_E4M3FN
+    nsplit = None
+    if args.splits is not None:
+        nsplit = args.splits or ha.attn_splitkv_auto_splits(w.B, w.Hq, w.Sq, w.Skv, w.D)
+        wbytes = ha.attn_splitkv_workspace_bytes(w.B, w.Hq, w.Sq, w.D, nsplit)
+        ws = torch.empty(max(wbytes, 16), dtype=torch.uint8, device=dev)
 
     def launch():
-        st = ha.attn_fwd(Q, K, V, O, L, w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.scale, int(causal), dt,
-                         ds[0], ds[1], ds[2], stream.cuda_stream)
+        if nsplit is None:
+            st = ha.attn_fwd(Q, K, V, O, L, w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.scale, int(causal), dt,
+                             ds[0], ds[1], ds[2], stream.cuda_stream)
+        else:
+            st = ha.attn_fwd_splitkv(Q, K, V, O, L, w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.scale, int(causal), dt,
+                                     ds[0], ds[1], ds[2], nsplit, ws, wbytes, stream.cuda_stream)
         if st != 0:
             raise ha.AttnError(st, "attn_fwd")
 
@@ -152,10 +161,11 @@ def bench_workload(args, w, make_inputs):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtn, "data": "synthetic",
         "config": {"workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Skv{w.Skv} D{w.D} "
-                               f"{'causal' if causal else 'non-causal'}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                               f"{'causal' if causal else 'non-causal'}"
+                               + (f", {nsplit} key splits" if nsplit else ""), "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "causal": causal},
         "ms_mean": round(float(tl.mean()) * 1e3, 4), "ms_p50": round(float(np.median(tl)) * 1e3, 4),
-        "frac_of_peak": round(tf / PEAK_TFLOPS[dtn], 4),
+        "frac_of_peak": round(tf / PEAK_TFLOPS[dtn], 4), "key_splits": nsplit or 1,
         "workgroups": w.B * w.Hq * ((w.Sq + 255) // 256)}), flush=True)
 
 
@@ -169,6 +179,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB each (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="with --workload: run attn_fwd_splitkv with this many key splits (0 = the "
+                         "library's choice) instead of attn_fwd")
     ap.add_argument("--workload", default=None,
                     help="time one other workload of synth.WORKLOADS instead (a context line, not the "
                          "headline); causal workloads run causal")

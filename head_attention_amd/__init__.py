@@ -2,12 +2,14 @@
 
 Argument marshalling only: every step of the attention runs in the HIP
 kernels behind the C ABI declared in ``include/attn.h``. The functions
-``attn_fwd``, ``attn_fwd_chunk``, ``attn_merge_lse2_host`` and
-``attn_status_string`` carry the C names and arguments one for one (pointer
-arguments accept a torch tensor, a plain integer address or None) and return
-the C status code. ``forward`` is a convenience wrapper over ``attn_fwd_chunk``
-that reads the sizes off torch tensors, allocates the outputs with torch and
-raises ``AttnError`` on a non-OK status.
+``attn_fwd``, ``attn_fwd_chunk``, ``attn_fwd_splitkv``,
+``attn_splitkv_workspace_bytes``, ``attn_splitkv_auto_splits``,
+``attn_merge_lse2_host`` and ``attn_status_string`` carry the C names and
+arguments one for one (pointer arguments accept a torch tensor, a plain integer
+address or None) and return what the C function returns. ``forward`` and
+``forward_splitkv`` are convenience wrappers that read the sizes off torch
+tensors, allocate the outputs (and the split workspace) with torch and raise
+``AttnError`` on a non-OK status.
 
 There is no fallback: if the library is missing, loading raises.
 """
@@ -18,8 +20,9 @@ import os
 
 __all__ = [
     "ATTN_BF16", "ATTN_FP8_E4M3FN", "STATUS", "AttnError", "lib", "library_path",
-    "attn_fwd", "attn_fwd_chunk", "attn_merge_lse2_host", "attn_status_string", "forward",
-    "merge_lse2_host",
+    "attn_fwd", "attn_fwd_chunk", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
+    "attn_splitkv_auto_splits", "attn_merge_lse2_host", "attn_status_string", "forward",
+    "forward_splitkv", "merge_lse2_host",
 ]
 
 ATTN_BF16 = 0
@@ -27,8 +30,10 @@ ATTN_FP8_E4M3FN = 1
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_HEAD_DIM", 4: "ATTN_ERR_DTYPE",
     5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_OVERFLOW", 7: "ATTN_ERR_SCALE", 8: "ATTN_ERR_HIP",
+    9: "ATTN_ERR_WORKSPACE",
 }
-EXPORTED = ("attn_fwd", "attn_fwd_chunk", "attn_merge_lse2_host", "attn_status_string")
+EXPORTED = ("attn_fwd", "attn_fwd_chunk", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
+            "attn_splitkv_auto_splits", "attn_merge_lse2_host", "attn_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libattn.so")
@@ -54,6 +59,12 @@ def lib():
         L.attn_fwd.restype = i32
         L.attn_fwd_chunk.argtypes = fwd_args + [i64, vp]
         L.attn_fwd_chunk.restype = i32
+        L.attn_fwd_splitkv.argtypes = fwd_args + [i64, vp, i64, vp]
+        L.attn_fwd_splitkv.restype = i32
+        L.attn_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+        L.attn_splitkv_workspace_bytes.restype = i64
+        L.attn_splitkv_auto_splits.argtypes = [i64, i64, i64, i64, i64]
+        L.attn_splitkv_auto_splits.restype = i64
         L.attn_merge_lse2_host.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64]
         L.attn_merge_lse2_host.restype = i32
         L.attn_status_string.argtypes = [i32]
@@ -98,6 +109,23 @@ def attn_fwd_chunk(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dty
                                 _stream(stream))
 
 
+def attn_fwd_splitkv(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype,
+                     q_descale=None, k_descale=None, v_descale=None, n_splits=0, workspace=None,
+                     workspace_bytes=0, stream=0):
+    return lib().attn_fwd_splitkv(_addr(q), _addr(k), _addr(v), _addr(out), _addr(lse), B, Hq, Hkv, Sq, Skv,
+                                  D, float(scale), int(bool(causal)), int(dtype),
+                                  _addr(q_descale), _addr(k_descale), _addr(v_descale), int(n_splits),
+                                  _addr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def attn_splitkv_workspace_bytes(B, Hq, Sq, D, n_splits):
+    return lib().attn_splitkv_workspace_bytes(B, Hq, Sq, D, n_splits)
+
+
+def attn_splitkv_auto_splits(B, Hq, Sq, Skv, D):
+    return lib().attn_splitkv_auto_splits(B, Hq, Sq, Skv, D)
+
+
 def attn_merge_lse2_host(o1, lse1, o2, lse2, o_out, lse_out, B, H, S, D):
     return lib().attn_merge_lse2_host(_addr(o1), _addr(lse1), _addr(o2), _addr(lse2), _addr(o_out),
                                       _addr(lse_out), B, H, S, D)
@@ -136,6 +164,44 @@ def forward(q, k, v, scale=None, causal=False, q_descale=None, k_descale=None, v
                         q_descale, k_descale, v_descale, kv_start, stream)
     if st != 0:
         raise AttnError(st, "attn_fwd_chunk")
+    return out, lse
+
+
+def forward_splitkv(q, k, v, n_splits=0, scale=None, causal=False, q_descale=None, k_descale=None,
+                    v_descale=None, out=None, lse=None, workspace=None, stream=None):
+    """(out, lse) like ``forward``, computed by ``attn_fwd_splitkv`` with n_splits key
+    splits (0: the library's choice). The fp32 split workspace is allocated with
+    torch unless one (a uint8 GPU tensor) is passed."""
+    import torch
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if q.dtype == torch.bfloat16:
+        dt = ATTN_BF16
+    elif q.dtype == torch.float8_e4m3fn:
+        dt = ATTN_FP8_E4M3FN
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for t in (q, k, v):
+        if t.dtype != q.dtype or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("q, k, v must be contiguous GPU tensors of one dtype")
+    if n_splits == 0:
+        n_splits = attn_splitkv_auto_splits(B, Hq, Sq, Skv, D)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = attn_splitkv_workspace_bytes(B, Hq, Sq, D, n_splits)
+    if need < 0:
+        raise AttnError(2, "attn_splitkv_workspace_bytes")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = attn_fwd_splitkv(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dt,
+                          q_descale, k_descale, v_descale, n_splits, workspace, wbytes, stream)
+    if st != 0:
+        raise AttnError(st, "attn_fwd_splitkv")
     return out, lse
 
 

@@ -59,6 +59,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kWaves = 8;
@@ -79,6 +80,12 @@ struct Params {
   const float* qd;
   const float* kd;
   const float* vd;
+  // Key splits: workgroup blockIdx.x / (B * Hq * n_qtiles) takes keys
+  // [split * split_len, + split_len). With o32 set, each split writes its
+  // normalised fp32 O and its LSE to o32 / lse32 at split * B*Hq*Sq rows.
+  int nsplit, split_len;
+  float* o32;
+  float* lse32;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -156,24 +163,30 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
 
   const int BH = p.B * p.Hq;
+  const int per_split = BH * p.n_qtiles;
+  const int split = (int)(blockIdx.x / per_split), bid = (int)(blockIdx.x % per_split);
   int bh, qt;
   if (CAUSAL) {  // longest rows first
-    qt = p.n_qtiles - 1 - (int)(blockIdx.x / BH);
-    bh = (int)(blockIdx.x % BH);
+    qt = p.n_qtiles - 1 - bid / BH;
+    bh = bid % BH;
   } else {
-    bh = (int)(blockIdx.x / p.n_qtiles);
-    qt = (int)(blockIdx.x % p.n_qtiles);
+    bh = bid / p.n_qtiles;
+    qt = bid % p.n_qtiles;
   }
+  // This workgroup's keys: [s0, s0 + Skv) of the head; causal positions shift by s0.
+  const int s0 = split * p.split_len;
+  const int Skv = max(0, min(p.Skv - s0, p.split_len));
+  const int kv_start = p.kv_start + s0;
   const int b = bh / p.Hq, h = bh % p.Hq, hk = h / p.group;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, n = lane & 31;
   const int q0 = qt * kBM, qw = q0 + wave * 32, qi = qw + n;
 
   const size_t qrow0 = (size_t)(b * p.Hq + h) * (size_t)p.Sq;
-  const size_t krow0 = (size_t)(b * p.Hkv + hk) * (size_t)p.Skv;
+  const size_t krow0 = (size_t)(b * p.Hkv + hk) * (size_t)p.Skv + (size_t)(Skv > 0 ? s0 : 0);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qrow0 * ROWB, (uint32_t)p.Sq * ROWB);
-  const i32x4 rk = rsrc_words(p.k + krow0 * ROWB, (uint32_t)p.Skv * ROWB);
-  const i32x4 rv = rsrc_words(p.v + krow0 * ROWB, (uint32_t)p.Skv * ROWB);
+  const i32x4 rk = rsrc_words(p.k + krow0 * ROWB, (uint32_t)Skv * ROWB);
+  const i32x4 rv = rsrc_words(p.v + krow0 * ROWB, (uint32_t)Skv * ROWB);
   const unsigned smem_addr = (unsigned)(uintptr_t)smem;
 
   float c = p.c, oscale = 1.f;
@@ -183,14 +196,12 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
     oscale = vd;
   }
 
-  const int Skv = p.Skv, kv_start = p.kv_start;   // read by the tile lambda (no argument struct capture)
-
   // Key tiles this workgroup needs, and those this wave needs.
   const int rows_end = min(q0 + kBM, p.Sq);
-  const int kv_end = CAUSAL ? min(p.Skv, max(0, rows_end - p.kv_start)) : p.Skv;
+  const int kv_end = CAUSAL ? min(Skv, max(0, rows_end - kv_start)) : Skv;
   const int ntiles = (kv_end + kBN - 1) / kBN;
   const bool wave_live = qw < p.Sq;
-  const int w_kv_end = CAUSAL ? min(p.Skv, max(0, min(qw + 32, p.Sq) - p.kv_start)) : p.Skv;
+  const int w_kv_end = CAUSAL ? min(Skv, max(0, min(qw + 32, p.Sq) - kv_start)) : Skv;
   const int w_ntiles = wave_live ? (w_kv_end + kBN - 1) / kBN : 0;
 
   // Q fragments (B operand of S^T = K Q^T); rows >= Sq read as zero.
@@ -428,21 +439,85 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   if (!wave_live) return;
   const float ltot = xor32_sum(l);
   const float inv = ltot > 0.f ? oscale / ltot : 0.f;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + qrow0 * (size_t)(D * 2), (uint32_t)p.Sq * D * 2);
+  const float lse = ltot > 0.f ? (m + __log2f(ltot) - kPre) * 0.69314718055994531f : -INFINITY;
+  if (p.o32 == nullptr) {
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + qrow0 * (size_t)(D * 2), (uint32_t)p.Sq * D * 2);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const u32x2 w = u32x2{pack_bf16(o[db][4 * ii + 0] * inv, o[db][4 * ii + 1] * inv),
-                            pack_bf16(o[db][4 * ii + 2] * inv, o[db][4 * ii + 3] * inv)};
-      const int col = 32 * db + 8 * ii + 4 * g;
-      __builtin_amdgcn_raw_buffer_store_b64(w, ro, (qi * D + col) * 2, 0, 0);
+      for (int ii = 0; ii < 4; ++ii) {
+        const u32x2 w = u32x2{pack_bf16(o[db][4 * ii + 0] * inv, o[db][4 * ii + 1] * inv),
+                              pack_bf16(o[db][4 * ii + 2] * inv, o[db][4 * ii + 3] * inv)};
+        const int col = 32 * db + 8 * ii + 4 * g;
+        __builtin_amdgcn_raw_buffer_store_b64(w, ro, (qi * D + col) * 2, 0, 0);
+      }
+    if (g == 0) {
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + qrow0, (uint32_t)p.Sq * 4);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
     }
-  if (g == 0) {
-    const float lse = ltot > 0.f ? (m + __log2f(ltot) - kPre) * 0.69314718055994531f : -INFINITY;
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + qrow0, (uint32_t)p.Sq * 4);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
+  } else {
+    // one key split: normalised fp32 O and the split's LSE, for the merge kernel
+    const size_t prow0 = (size_t)split * (size_t)BH * (size_t)p.Sq + qrow0;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o32 + prow0 * D, (uint32_t)p.Sq * D * 4);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const u32x4 w = u32x4{__float_as_uint(o[db][4 * ii + 0] * inv), __float_as_uint(o[db][4 * ii + 1] * inv),
+                              __float_as_uint(o[db][4 * ii + 2] * inv), __float_as_uint(o[db][4 * ii + 3] * inv)};
+        const int col = 32 * db + 8 * ii + 4 * g;
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, (qi * D + col) * 4, 0, 0);
+      }
+    if (g == 0) {
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse32 + prow0, (uint32_t)p.Sq * 4);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
+    }
   }
+}
+
+// Merge of the key splits of attn_fwd_splitkv: for each row, L = ln sum_s
+// e^(L_s) and O = sum_s e^(L_s - L) O_s (fp32, bf16 out); rows whose splits
+// are all empty (L_s = -inf) get O = 0 and L = -inf. Sixteen lanes per row,
+// eight columns each (D = 128) or four (D = 64).
+template <int D>
+__global__ void __launch_bounds__(256) merge_splits_kernel(const float* __restrict__ o32, const float* __restrict__ lse32,
+                                                           char* __restrict__ out, float* __restrict__ lse,
+                                                           long long rows, int nsplit) {
+  constexpr int PER = D / 16;                    // columns per lane
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, lse32[(long long)sp * rows + row]);
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  float tot = 0.f;
+  if (mx != -INFINITY) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float w = __builtin_amdgcn_exp2f((lse32[(long long)sp * rows + row] - mx) * kLog2e);   // 0 for an empty split
+      tot += w;
+      const float* src = o32 + ((long long)sp * rows + row) * D + part * PER;
+#pragma unroll
+      for (int j = 0; j < PER; j += 4) {
+        const f32x4 x = *(const f32x4*)(src + j);
+        acc[j] += w * x[0];
+        acc[j + 1] += w * x[1];
+        acc[j + 2] += w * x[2];
+        acc[j + 3] += w * x[3];
+      }
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  unsigned pk[PER / 2];
+#pragma unroll
+  for (int j = 0; j < PER / 2; ++j) pk[j] = pack_bf16(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+  if constexpr (PER == 8)
+    *(u32x4*)(out + (row * D + part * PER) * 2) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+  else
+    *(u32x2*)(out + (row * D + part * PER) * 2) = u32x2{pk[0], pk[1]};
+  if (part == 0) lse[row] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
 }
 
 typedef void (*kernel_fn)(Params);
@@ -456,11 +531,17 @@ kernel_fn pick(bool causal) {
 
 using namespace hat;
 
+static constexpr int64_t kMaxSplits = 256;
+
+static int64_t splitkv_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t D, int64_t nsplit) {
+  return nsplit <= 1 ? 0 : nsplit * B * Hq * Sq * (D + 1) * 4;
+}
+
 static attn_status_t launch(const void* q, const void* k, const void* v, void* out, float* lse,
                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
                             float scale, int causal, attn_dtype_t dtype,
                             const float* qd, const float* kd, const float* vd, int64_t kv_start,
-                            void* stream) {
+                            int64_t nsplit, void* workspace, int64_t workspace_bytes, void* stream) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3FN) return ATTN_ERR_DTYPE;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || kv_start < 0) return ATTN_ERR_SHAPE;
@@ -479,8 +560,20 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   const int64_t lim = (int64_t)1 << 31;
   if ((Sq + kBM) * D * 2 >= lim || (Skv + kBN) * rowb >= lim || Sq + kBM >= lim || kv_start >= lim) return ATTN_ERR_OVERFLOW;
   const int64_t n_qtiles = (Sq + kBM - 1) / kBM;
-  const int64_t grid = B * Hq * n_qtiles;
-  if (B * Hq >= lim || grid >= lim) return ATTN_ERR_OVERFLOW;
+  if (nsplit < 1 || nsplit > kMaxSplits) return ATTN_ERR_SHAPE;
+  // Key splits are whole tiles; fewer tiles than splits leaves fewer splits.
+  const int64_t ktiles = any_kv ? (Skv + kBN - 1) / kBN : 0;
+  const int64_t per = ktiles > 0 ? (ktiles + nsplit - 1) / nsplit : 1;
+  const int64_t nsp = ktiles > 0 ? (ktiles + per - 1) / per : 1;
+  const int64_t rows = B * Hq * Sq;
+  if (nsp > 1) {
+    if (!workspace) return ATTN_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 15) return ATTN_ERR_WORKSPACE;
+    if (workspace_bytes < splitkv_bytes(B, Hq, Sq, D, nsp)) return ATTN_ERR_WORKSPACE;
+    if ((Sq + kBM) * D * 4 >= lim) return ATTN_ERR_OVERFLOW;
+  }
+  const int64_t grid = B * Hq * n_qtiles * nsp;
+  if (B * Hq >= lim || grid >= lim || (rows + 16) / 16 >= lim) return ATTN_ERR_OVERFLOW;
 
   Params p;
   p.q = (const char*)q;
@@ -500,12 +593,48 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   p.qd = dtype == ATTN_FP8_E4M3FN ? qd : nullptr;
   p.kd = dtype == ATTN_FP8_E4M3FN ? kd : nullptr;
   p.vd = dtype == ATTN_FP8_E4M3FN ? vd : nullptr;
+  p.nsplit = (int)nsp;
+  p.split_len = nsp > 1 ? (int)(per * kBN) : (int)Skv;
+  p.o32 = nsp > 1 ? (float*)workspace : nullptr;
+  p.lse32 = nsp > 1 ? (float*)workspace + nsp * rows * D : nullptr;
 
   kernel_fn fn;
   if (dtype == ATTN_BF16) fn = D == 128 ? pick<128, false>(causal) : pick<64, false>(causal);
   else fn = D == 128 ? pick<128, true>(causal) : pick<64, true>(causal);
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+  if (nsp > 1) {
+    const unsigned mgrid = (unsigned)((rows + 15) / 16);
+    if (D == 128)
+      hipLaunchKernelGGL(merge_splits_kernel<128>, dim3(mgrid), dim3(256), 0, (hipStream_t)stream,
+                         p.o32, p.lse32, (char*)out, lse, (long long)rows, (int)nsp);
+    else
+      hipLaunchKernelGGL(merge_splits_kernel<64>, dim3(mgrid), dim3(256), 0, (hipStream_t)stream,
+                         p.o32, p.lse32, (char*)out, lse, (long long)rows, (int)nsp);
+    if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+// Key splits for a grid that leaves compute units idle: none when the query
+// tiles already occupy at least 85 % of the last round of workgroups (the
+// chip is power-bound, so idle CUs cost little); else the fewest splits, each
+// of at least 16 key tiles, that bring the rounds to 90 % occupancy (merge
+// traffic and per-workgroup start-up grow with the split count).
+static int64_t auto_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t nwg = B * Hq * ((Sq + kBM - 1) / kBM);
+  const int64_t ktiles = (Skv + kBN - 1) / kBN;
+  auto occupancy = [&](int64_t sp) {
+    const int64_t w = nwg * sp;
+    return (double)w / (double)(cus * ((w + cus - 1) / cus));
+  };
+  if (nwg <= 0 || occupancy(1) >= 0.85) return 1;
+  for (int64_t sp = 2; sp <= 16 && ktiles / sp >= 16; ++sp)
+    if (occupancy(sp) >= 0.9) return sp;
+  return 1;
 }
 
 extern "C" attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -514,7 +643,7 @@ extern "C" attn_status_t attn_fwd(const void* q, const void* k, const void* v, v
                                   const float* q_descale, const float* k_descale, const float* v_descale,
                                   void* stream) {
   return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, q_descale, k_descale,
-                v_descale, 0, stream);
+                v_descale, 0, 1, nullptr, 0, stream);
 }
 
 extern "C" attn_status_t attn_fwd_chunk(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -523,5 +652,26 @@ extern "C" attn_status_t attn_fwd_chunk(const void* q, const void* k, const void
                                         const float* q_descale, const float* k_descale,
                                         const float* v_descale, int64_t kv_start, void* stream) {
   return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, q_descale, k_descale,
-                v_descale, kv_start, stream);
+                v_descale, kv_start, 1, nullptr, 0, stream);
+}
+
+extern "C" int64_t attn_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int64_t D) {
+  if (B < 0 || Hq < 0 || Sq < 0 || Skv < 0 || (D != 64 && D != 128)) return -1;
+  return auto_splits(B, Hq, Sq, Skv);
+}
+
+extern "C" int64_t attn_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t D, int64_t n_splits) {
+  if (B < 0 || Hq < 0 || Sq < 0 || (D != 64 && D != 128) || n_splits < 0 || n_splits > kMaxSplits) return -1;
+  return splitkv_bytes(B, Hq, Sq, D, n_splits);
+}
+
+extern "C" attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                                          float scale, int causal, attn_dtype_t dtype,
+                                          const float* q_descale, const float* k_descale, const float* v_descale,
+                                          int64_t n_splits, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (n_splits < 0) return ATTN_ERR_SHAPE;
+  if (n_splits == 0) n_splits = (B > 0 && Hq > 0 && Sq > 0 && Skv > 0) ? auto_splits(B, Hq, Sq, Skv) : 1;
+  return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, q_descale, k_descale,
+                v_descale, 0, n_splits, workspace, workspace_bytes, stream);
 }

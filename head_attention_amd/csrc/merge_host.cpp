@@ -65,13 +65,14 @@ extern "C" const char* attn_status_string(attn_status_t s) {
   switch (s) {
     case ATTN_OK: return "ATTN_OK";
     case ATTN_ERR_NULL: return "ATTN_ERR_NULL: a required pointer is NULL";
-    case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE: negative size, or Hq not a multiple of Hkv, or kv_start < 0";
+    case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE: negative size, Hq not a multiple of Hkv, kv_start < 0, or a bad split count";
     case ATTN_ERR_HEAD_DIM: return "ATTN_ERR_HEAD_DIM: head dimension must be 64 or 128";
     case ATTN_ERR_DTYPE: return "ATTN_ERR_DTYPE: unknown input dtype";
     case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN: q/k/v/out must be 16-byte aligned, lse 4-byte aligned";
     case ATTN_ERR_OVERFLOW: return "ATTN_ERR_OVERFLOW: a head slice or the grid exceeds 32-bit addressing";
     case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE: scale must be finite and > 0";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: kernel launch failed";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: split-KV workspace missing, misaligned or too small";
   }
   return "ATTN_ERR_UNKNOWN";
 }

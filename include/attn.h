@@ -52,13 +52,14 @@ typedef enum {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,      /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = 2,     /* a negative size, Hkv = 0 with Hq > 0, Hq % Hkv != 0, kv_start < 0 */
+  ATTN_ERR_SHAPE = 2,     /* a negative size, Hkv = 0 with Hq > 0, Hq % Hkv != 0, kv_start < 0, n_splits outside 0..256 */
   ATTN_ERR_HEAD_DIM = 3,  /* D is not 64 or 128 */
   ATTN_ERR_DTYPE = 4,     /* unknown attn_dtype_t */
   ATTN_ERR_ALIGN = 5,     /* q, k, v or out not 16-byte aligned, or lse not 4-byte aligned */
   ATTN_ERR_OVERFLOW = 6,  /* one head's slice reaches 2^31 bytes, or the grid is too large */
   ATTN_ERR_SCALE = 7,     /* scale is not finite or not > 0 */
-  ATTN_ERR_HIP = 8        /* the kernel launch failed */
+  ATTN_ERR_HIP = 8,       /* the kernel launch failed */
+  ATTN_ERR_WORKSPACE = 9  /* attn_fwd_splitkv: workspace NULL, not 16-byte aligned, or too small */
 } attn_status_t;
 
 /*
@@ -115,6 +116,47 @@ attn_status_t attn_merge_lse2_host(const uint16_t* o1, const float* lse1,
                                    const uint16_t* o2, const float* lse2,
                                    uint16_t* o_out, float* lse_out,
                                    int64_t B, int64_t H, int64_t S, int64_t D);
+
+/*
+ * attn_fwd_splitkv — attn_fwd with the keys split over n_splits workgroup
+ * sets, for shapes whose B * Hq * ceil(Sq / 256) query tiles leave the GPU's
+ * compute units idle (few heads, short Sq against a long Skv). Each split
+ * computes the (O, LSE) of its key range — the chunk semantics of
+ * attn_fwd_chunk — into the caller's workspace as fp32, and a second kernel on
+ * the same stream merges them by LSE into out (bf16) and lse, the N-way form
+ * of the out/LSE merge on the page "feat(attention): add strict bitwise ROCm
+ * path" (Summary table, CP communication). Results equal attn_fwd's up to
+ * fp32 rounding of the partial sums.
+ *
+ *   n_splits        >= 1 splits of whole 64-key tiles (fewer are used when Skv
+ *                   has fewer tiles); 1 is attn_fwd itself (no workspace is
+ *                   read). 0 lets the library choose
+ *                   (attn_splitkv_auto_splits). At most 256.
+ *   workspace       device buffer of at least attn_splitkv_workspace_bytes(B,
+ *                   Hq, Sq, D, n_splits) bytes, 16-byte aligned, owned by the
+ *                   caller; its contents on entry do not matter and are
+ *                   overwritten. It may be NULL when one split is used.
+ *   workspace_bytes its size in bytes.
+ * Other arguments, layouts and errors as attn_fwd; ATTN_ERR_WORKSPACE when a
+ * workspace is needed and is missing, misaligned or too small. Two calls that
+ * overlap in time must not share a workspace.
+ */
+attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                               float scale, int causal, attn_dtype_t dtype,
+                               const float* q_descale, const float* k_descale, const float* v_descale,
+                               int64_t n_splits, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_fwd_splitkv needs for n_splits (0 when n_splits <= 1;
+ * n_splits * B * Hq * Sq * (D + 1) * 4), or -1 on invalid arguments. */
+int64_t attn_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t D, int64_t n_splits);
+
+/* The split count attn_fwd_splitkv uses for n_splits = 0 on the current
+ * device: 1 when the B * Hq * ceil(Sq / 256) query tiles already fill at
+ * least 85 % of their last round over the compute units, else the fewest
+ * splits (each at least 16 key tiles, at most 16) that reach 90 %, or 1 if
+ * none does. -1 on invalid arguments. Queries the current HIP device. */
+int64_t attn_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int64_t D);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_status_string(attn_status_t s);

@@ -71,6 +71,9 @@ WORKLOADS = {
                  note="cross-attention, 90000 queries against 512 keys, 40 heads"),
         Workload(8, "wan_cross_fp8", 1, 40, 40, 90000, 512, 128, "e4m3fn", (False,),
                  note="the same cross-attention in fp8 e4m3fn with per-tensor descales"),
+        Workload(9, "video_dit_shard", 1, 5, 5, 9450, 75600, 128, "bf16", (False,),
+                 note="one eighth of the video-DiT queries against all its keys (one GPU's share "
+                      "when the queries are split over eight GPUs)"),
     ]
 }
 

@@ -80,6 +80,44 @@ def test_fail_closed_validation(L, args, status):
     assert st == status, (args, ha.STATUS.get(st, st))
 
 
+@pytest.mark.parametrize("args,status", [
+    (dict(n_splits=-1), 2),
+    (dict(n_splits=257), 2),
+    (dict(n_splits=2, workspace=None), 9),
+    (dict(n_splits=2, workspace=P + 8), 9),
+    (dict(n_splits=2, wbytes=100), 9),
+    (dict(n_splits=2, D=96), 3),
+    (dict(n_splits=2, q=None), 1),
+])
+def test_splitkv_fail_closed_validation(L, args, status):
+    a = dict(q=P, k=P, v=P, out=P, lse=P, B=1, Hq=4, Hkv=2, Sq=100, Skv=1000, D=128, n_splits=2,
+             workspace=P, wbytes=1 << 40)
+    a.update(args)
+    st = ha.attn_fwd_splitkv(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
+                             a["Skv"], a["D"], 0.1, 0, 0, None, None, None, a["n_splits"], a["workspace"],
+                             a["wbytes"], 0)
+    assert st == status, (args, ha.STATUS.get(st, st))
+
+
+def test_splitkv_workspace_size():
+    assert ha.attn_splitkv_workspace_bytes(2, 3, 100, 128, 1) == 0
+    assert ha.attn_splitkv_workspace_bytes(2, 3, 100, 128, 4) == 4 * 2 * 3 * 100 * 129 * 4
+    assert ha.attn_splitkv_workspace_bytes(1, 1, 10, 64, 2) == 2 * 10 * 65 * 4
+    assert ha.attn_splitkv_workspace_bytes(1, 1, 10, 96, 2) == -1
+    assert ha.attn_splitkv_workspace_bytes(1, 1, 10, 128, 300) == -1
+
+
+def test_splitkv_auto_split_choice():
+    # 1480 video-DiT workgroups fill 256 CUs, 228 (window-30 shape) nearly do: no split.
+    assert ha.attn_splitkv_auto_splits(1, 5, 75600, 75600, 128) == 1
+    assert ha.attn_splitkv_auto_splits(1, 12, 4680, 51480, 128) == 1
+    # 185 (an eighth of the video-DiT queries) fill 72 %: four splits make 740 = 96 % of 3 rounds.
+    assert ha.attn_splitkv_auto_splits(1, 5, 9450, 75600, 128) == 4
+    assert ha.attn_splitkv_auto_splits(2, 8, 2048, 2048, 128) == 2
+    assert ha.attn_splitkv_auto_splits(1, 1, 256, 512, 128) == 1      # too few key tiles to split
+    assert ha.attn_splitkv_auto_splits(1, 1, 256, 96, 100) == -1
+
+
 def test_zero_queries_return_ok_without_launch(L):
     assert ha.attn_fwd(None, None, None, None, None, 1, 4, 2, 0, 100, 128, 0.1, 0, 0) == 0
     assert ha.attn_fwd(None, None, None, None, None, 0, 4, 2, 10, 100, 128, 0.1, 0, 0) == 0

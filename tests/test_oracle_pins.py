@@ -191,6 +191,20 @@ def test_chunked_keys_merged_by_lse_equal_unsplit(causal, split):
     np.testing.assert_allclose(Lm, L, rtol=1e-13, atol=1e-14)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bounds", [(0, 5, 11, 30), (0, 1, 2, 3, 30), (0, 29, 30), (0, 10, 10, 20, 30)])
+def test_n_way_key_split_merged_by_lse_equals_unsplit(causal, bounds):
+    """N key ranges (including an empty one), each with its absolute start, merged by LSE."""
+    Hq, Hkv, S, D = 4, 2, 30, 8
+    q, k, v = rand(1, Hq, S, D), rand(1, Hkv, S, D), rand(1, Hkv, S, D)
+    O, L = attention_forward(q, k, v, 0.6, causal)
+    parts = [attention_forward(q, k[:, :, a:b], v[:, :, a:b], 0.6, causal, kv_start=a)
+             for a, b in zip(bounds[:-1], bounds[1:])]
+    Om, Lm = merge_lse(parts)
+    np.testing.assert_allclose(Om, O, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(Lm, L, rtol=1e-13, atol=1e-14)
+
+
 def test_merge_of_empty_chunks():
     O1, L1 = np.zeros((3, 2)), np.full(3, -np.inf)
     O2, L2 = rand(3, 2), np.array([-np.inf, 0.5, 2.0])
