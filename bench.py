@@ -46,6 +46,25 @@ def pages_gbps(B, Hq, Hkv, Sq, Skv, D, elt, seconds):
     return n * elt / seconds / 1e9
 
 
+def allowed_pairs(Sq, Skv, causal, window_left=-1, window_right=-1, sink=0):
+    """Number of (query, key) pairs local attention keeps, counted row by row
+    (key j is kept for query i iff it is inside [i - left, i + right] or j < sink,
+    and j <= i with causal)."""
+    import numpy as np
+    i = np.arange(Sq, dtype=np.int64)
+    lo = np.maximum(0, i - window_left) if window_left >= 0 else np.zeros_like(i)
+    hi = np.minimum(Skv - 1, i + window_right) if window_right >= 0 else np.full_like(i, Skv - 1)
+    if causal:
+        hi = np.minimum(hi, i)
+    win = np.maximum(0, hi - lo + 1)
+    s_hi = np.minimum(sink, Skv) - 1                      # sink keys [0, s_hi]
+    if causal:
+        s_hi = np.minimum(s_hi, i)
+    snk = np.maximum(0, s_hi + 1)
+    both = np.maximum(0, np.minimum(hi, s_hi) - lo + 1)   # sink keys already inside the window
+    return int((win + snk - np.minimum(both, np.minimum(win, snk))).sum())
+
+
 def algorithmic_bytes(B, Hq, Hkv, Sq, Skv, D, elt):
     """Compulsory HBM traffic of one launch: Q, K, V read once; O (bf16) and LSE (fp32) written once."""
     return (B * Hq * Sq * D + 2 * B * Hkv * Skv * D) * elt + B * Hq * Sq * D * 2 + B * Hq * Sq * 4
@@ -131,8 +150,16 @@ def bench_workload(args, w, make_inputs):
         wbytes = ha.attn_splitkv_workspace_bytes(w.B, w.Hq, w.Sq, w.D, nsplit)
         ws = torch.empty(max(wbytes, 16), dtype=torch.uint8, device=dev)
 
+    local = w.window_left >= 0 or w.window_right >= 0 or w.sink > 0
+    if local and nsplit is not None:
+        raise SystemExit("--splits does not apply to a local-attention workload")
+
     def launch():
-        if nsplit is None:
+        if local:
+            st = ha.attn_fwd_window(Q, K, V, O, L, w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.scale, int(causal), dt,
+                                    ds[0], ds[1], ds[2], 0, w.window_left, w.window_right, w.sink,
+                                    stream.cuda_stream)
+        elif nsplit is None:
             st = ha.attn_fwd(Q, K, V, O, L, w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.scale, int(causal), dt,
                              ds[0], ds[1], ds[2], stream.cuda_stream)
         else:
@@ -153,7 +180,10 @@ def bench_workload(args, w, make_inputs):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     tl = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
-    flops = attn_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, causal)
+    if local:   # 4*D flops per kept (query, key) pair
+        flops = 4.0 * w.B * w.Hq * w.D * allowed_pairs(w.Sq, w.Skv, causal, w.window_left, w.window_right, w.sink)
+    else:
+        flops = attn_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, causal)
     tf = flops / tl.mean() / 1e12
     dtn = "bf16" if fmt == "bf16" else "fp8"
     print(json.dumps({
@@ -162,8 +192,10 @@ def bench_workload(args, w, make_inputs):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtn, "data": "synthetic",
         "config": {"workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Skv{w.Skv} D{w.D} "
                                f"{'causal' if causal else 'non-causal'}"
+                               + (f", window {w.window_left}/{w.window_right}, sink {w.sink}" if local else "")
                                + (f", {nsplit} key splits" if nsplit else ""), "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "causal": causal},
+                   "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "causal": causal,
+                   **({"window_left": w.window_left, "window_right": w.window_right, "sink": w.sink} if local else {})},
         "ms_mean": round(float(tl.mean()) * 1e3, 4), "ms_p50": round(float(np.median(tl)) * 1e3, 4),
         "frac_of_peak": round(tf / PEAK_TFLOPS[dtn], 4), "key_splits": nsplit or 1,
         "workgroups": w.B * w.Hq * ((w.Sq + 255) // 256)}), flush=True)

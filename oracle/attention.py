@@ -25,6 +25,9 @@ Readings where the pages are silent (each listed in the design notes):
   with an explicit key offset for chunked calls).
 * A row with no allowed key has O = 0 and LSE = -inf.
 * Query head h reads KV head h // (Hq / Hkv).
+* Local attention: window sides and sink count are in key positions (the
+  same absolute positions as the causal test); a key is kept if it is inside
+  the window or is a sink key, and causal applies on top of both.
 
 Query rows are processed in independent blocks purely to bound memory (one
 fp64 score row at 75600 keys is 605 KB); no sum is split or reordered by it.
@@ -45,13 +48,22 @@ def _check_shapes(q, k, v):
     return B, Hq, Hkv, Sq, Skv, D
 
 
-def attention_forward(q, k, v, scale, causal=False, kv_start=0, rows=None, row_block=512):
+def attention_forward(q, k, v, scale, causal=False, kv_start=0, rows=None, row_block=512,
+                      window_left=-1, window_right=-1, sink=0):
     """Attention forward in float64.
 
     q: [B, Hq, Sq, D], k and v: [B, Hkv, Skv, D], real values (already
     dequantised). ``rows`` optionally selects a subset of query rows (an index
     array into Sq); each output row depends only on its own query, so a subset is
     the same computation restricted to those rows.
+
+    Local attention (window_size_left / window_size_right of the fmha_v3_fwd
+    call on the page "F8 fmha ASM gfx950", Test Result section; window and sink
+    settings of the page "[Proposal] ROCm (AMD Instinct) support for the core
+    attention and distributed init"): with key position j = key index +
+    kv_start, key j is allowed for query i iff it lies in the window
+    [i - window_left, i + window_right] (a side of -1 is unbounded) or j < sink;
+    causal additionally requires j <= i.
 
     Returns (O [B, Hq, R, D], LSE [B, Hq, R]) with R = Sq or len(rows).
     """
@@ -61,6 +73,9 @@ def attention_forward(q, k, v, scale, causal=False, kv_start=0, rows=None, row_b
     B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
     if kv_start < 0:
         raise ValueError("kv_start must be >= 0")
+    if window_left < -1 or window_right < -1 or sink < 0:
+        raise ValueError("window sides must be >= -1 and sink >= 0")
+    local = window_left >= 0 or window_right >= 0 or sink > 0
     group = Hq // Hkv
     row_idx = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
     R = row_idx.shape[0]
@@ -78,6 +93,13 @@ def attention_forward(q, k, v, scale, causal=False, kv_start=0, rows=None, row_b
                 if causal:
                     allowed = key_pos[None, :] <= ridx[:, None]
                     s = np.where(allowed, s, -np.inf)
+                if local:
+                    in_win = np.ones((len(ridx), Skv), dtype=bool)
+                    if window_left >= 0:
+                        in_win &= key_pos[None, :] >= ridx[:, None] - int(window_left)
+                    if window_right >= 0:
+                        in_win &= key_pos[None, :] <= ridx[:, None] + int(window_right)
+                    s = np.where(in_win | (key_pos[None, :] < int(sink)), s, -np.inf)
                 m = s.max(axis=1) if Skv > 0 else np.full(len(ridx), -np.inf)
                 live = np.isfinite(m)
                 p = np.exp(s[live] - m[live, None])               # exp(-inf) = 0 for masked

@@ -12,7 +12,7 @@ Inputs are nested lists (or anything indexable) of real numbers.
 import math
 
 
-def attention_brute(q, k, v, scale, causal=False, kv_start=0):
+def attention_brute(q, k, v, scale, causal=False, kv_start=0, window_left=-1, window_right=-1, sink=0):
     B, Hq, Sq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
     Hkv, Skv = len(k[0]), len(k[0][0])
     group = Hq // Hkv
@@ -22,7 +22,15 @@ def attention_brute(q, k, v, scale, causal=False, kv_start=0):
         for h in range(Hq):
             hk = h // group
             for i in range(Sq):
-                keys = [j for j in range(Skv) if (not causal) or (j + kv_start <= i)]
+                keys = []
+                for j in range(Skv):
+                    pos = j + kv_start
+                    if causal and pos > i:
+                        continue
+                    lo_ok = window_left < 0 or pos >= i - window_left
+                    hi_ok = window_right < 0 or pos <= i + window_right
+                    if (lo_ok and hi_ok) or pos < sink:
+                        keys.append(j)
                 if not keys:
                     continue
                 e = [math.exp(scale * math.fsum(q[b][h][i][d] * k[b][hk][j][d] for d in range(D)))

@@ -21,6 +21,14 @@ have Sq != Skv: the window-30 shape of the page "[Proposal] ROCm (AMD
 Instinct) support for the core attention and distributed init" (query 4680 x
 key 51480, 12 heads), and the cross-attention of the page "F8 fmha ASM gfx950"
 (90000 queries against 512 keys, 40 heads; an even head count), bf16 and fp8.
+
+Two local-attention workloads carry a window and sink keys (the pages give
+window / sink configurations, in video frames, but no token counts, so these
+sizes are chosen here): "swa_llm", causal GQA with the 32/8 heads of the
+pages' Qwen3-8B validation, 16384 tokens, a 4096-token sliding window
+(window_left 4095) and 4 sink tokens; and "video_band", the video-DiT shape
+(75600 tokens = 21 frames of 3600) with a band of three frames on either side
+(window 10800 / 10800) and the first frame as sinks (3600).
 """
 
 from dataclasses import dataclass, field
@@ -44,6 +52,9 @@ class Workload:
     causal: tuple = (False,)
     chunks: tuple = ()           # key chunk lengths for the chunked-merge run
     note: str = ""
+    window_left: int = -1        # local attention: -1 = unbounded side
+    window_right: int = -1
+    sink: int = 0
 
     @property
     def scale(self) -> float:
@@ -74,6 +85,12 @@ WORKLOADS = {
         Workload(9, "video_dit_shard", 1, 5, 5, 9450, 75600, 128, "bf16", (False,),
                  note="one eighth of the video-DiT queries against all its keys (one GPU's share "
                       "when the queries are split over eight GPUs)"),
+        Workload(10, "swa_llm", 1, 32, 8, 16384, 16384, 128, "bf16", (True,),
+                 note="causal sliding window of 4096 tokens with 4 sink tokens, GQA 32/8",
+                 window_left=4095, sink=4),
+        Workload(11, "video_band", 1, 5, 5, 75600, 75600, 128, "bf16", (False,),
+                 note="video-DiT shape with a +/-3-frame band and the first frame as sinks",
+                 window_left=10800, window_right=10800, sink=3600),
     ]
 }
 

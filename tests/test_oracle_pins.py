@@ -227,6 +227,94 @@ def test_row_subset_equals_full():
     np.testing.assert_array_equal(Ls, L[:, :, rows])
 
 
+# ---------------------------------------------------------------- local attention (window, sink)
+
+WINDOWS = [(-1, -1, 0), (0, 0, 0), (2, -1, 0), (-1, 1, 0), (1, 2, 0), (3, 0, 1), (0, 0, 2), (-1, -1, 3), (6, 6, 0)]
+
+
+@pytest.mark.parametrize("wl,wr,sink", WINDOWS)
+@pytest.mark.parametrize("causal,kv_start", [(False, 0), (True, 0), (False, 3), (True, 2)])
+def test_local_attention_matches_brute_force(wl, wr, sink, causal, kv_start):
+    Hq, Hkv, Sq, Skv, D = 4, 2, 9, 7, 3
+    q, k, v = rand(1, Hq, Sq, D), rand(1, Hkv, Skv, D), rand(1, Hkv, Skv, D)
+    O, L = attention_forward(q, k, v, 0.7, causal, kv_start, window_left=wl, window_right=wr, sink=sink)
+    Ob, Lb = attention_brute(q.tolist(), k.tolist(), v.tolist(), 0.7, causal, kv_start, wl, wr, sink)
+    np.testing.assert_allclose(O, np.array(Ob), rtol=1e-12, atol=1e-13)
+    Lb = np.array(Lb)
+    assert np.array_equal(np.isinf(L), np.isinf(Lb))
+    np.testing.assert_allclose(L[np.isfinite(L)], Lb[np.isfinite(Lb)], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("wl,wr,sink,causal", [(4, 2, 0, False), (5, -1, 2, True), (0, 3, 1, False)])
+def test_local_attention_matches_torch_sdpa_with_band_mask(wl, wr, sink, causal):
+    """torch's SDPA with an explicit boolean band mask built from index arithmetic."""
+    S, D = 40, 8
+    q, k, v = rand(1, 2, S, D), rand(1, 2, S, D), rand(1, 2, S, D)
+    O, L = attention_forward(q, k, v, 0.5, causal, window_left=wl, window_right=wr, sink=sink)
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    band = torch.ones(S, S, dtype=torch.bool)
+    if wl >= 0:
+        band &= j >= i - wl
+    if wr >= 0:
+        band &= j <= i + wr
+    mask = band | (j < sink)
+    if causal:
+        mask &= j <= i
+    Ot = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),
+                                                          torch.from_numpy(v), attn_mask=mask, scale=0.5)
+    np.testing.assert_allclose(O, Ot.numpy(), rtol=1e-12, atol=1e-13)
+    s = (0.5 * (torch.from_numpy(q) @ torch.from_numpy(k).transpose(-1, -2))).masked_fill(~mask, -math.inf)
+    np.testing.assert_allclose(L, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_zero_width_window_picks_own_key():
+    """A window of width zero keeps exactly key i for query i: O_i = v_i, LSE_i = scale q_i.k_i;
+    with one sink key as well, row i > 0 is the two-key softmax of keys 0 and i."""
+    S, D = 12, 5
+    q, k, v = rand(1, 1, S, D), rand(1, 1, S + 3, D), rand(1, 1, S + 3, D)
+    O, L = attention_forward(q, k, v, 0.9, window_left=0, window_right=0)
+    np.testing.assert_array_equal(O[0, 0], v[0, 0, :S])
+    np.testing.assert_allclose(L[0, 0], 0.9 * np.einsum("id,id->i", q[0, 0], k[0, 0, :S]), rtol=1e-14)
+    O, L = attention_forward(q, k, v, 0.9, window_left=0, window_right=0, sink=1)
+    for i in range(1, S):
+        s0, si = 0.9 * q[0, 0, i] @ k[0, 0, 0], 0.9 * q[0, 0, i] @ k[0, 0, i]
+        w0 = 1.0 / (1.0 + math.exp(si - s0))
+        np.testing.assert_allclose(O[0, 0, i], w0 * v[0, 0, 0] + (1 - w0) * v[0, 0, i], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(L[0, 0, i], np.logaddexp(s0, si), rtol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_covering_every_key_is_full_attention(causal):
+    Sq, Skv, D = 11, 17, 4
+    q, k, v = rand(1, 2, Sq, D), rand(1, 2, Skv, D), rand(1, 2, Skv, D)
+    O, L = attention_forward(q, k, v, 0.6, causal)
+    for wl, wr, sink in [(Sq, Skv, 0), (10 ** 6, 10 ** 6, 0), (-1, -1, Skv), (0, 0, Skv)]:
+        Ow, Lw = attention_forward(q, k, v, 0.6, causal, window_left=wl, window_right=wr, sink=sink)
+        np.testing.assert_array_equal(Ow, O)
+        np.testing.assert_array_equal(Lw, L)
+    # under causal, a right side >= 0 changes nothing
+    if causal:
+        Ow, Lw = attention_forward(q, k, v, 0.6, True, window_left=3, window_right=0)
+        Ox, Lx = attention_forward(q, k, v, 0.6, True, window_left=3, window_right=-1)
+        np.testing.assert_array_equal(Ow, Ox)
+        np.testing.assert_array_equal(Lw, Lx)
+
+
+@pytest.mark.parametrize("wl,wr,sink,causal", [(4, 4, 0, False), (6, -1, 2, True), (-1, 2, 3, False)])
+def test_local_attention_key_chunks_merged_by_lse_equal_unsplit(wl, wr, sink, causal):
+    """Window and sink are functions of absolute key position, so chunks with kv_start merge exactly."""
+    Hq, Hkv, S, D = 2, 1, 30, 6
+    q, k, v = rand(1, Hq, S, D), rand(1, Hkv, S, D), rand(1, Hkv, S, D)
+    kw = dict(window_left=wl, window_right=wr, sink=sink)
+    O, L = attention_forward(q, k, v, 0.6, causal, **kw)
+    parts = [attention_forward(q, k[:, :, a:b], v[:, :, a:b], 0.6, causal, kv_start=a, **kw)
+             for a, b in [(0, 2), (2, 13), (13, 30)]]
+    Om, Lm = merge_lse(parts)
+    np.testing.assert_allclose(Om, O, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(Lm, L, rtol=1e-13, atol=1e-14)
+
+
 # ---------------------------------------------------------------- the pages' printed figures
 
 def test_metric_arithmetic_reproduces_printed_summary():
@@ -237,6 +325,18 @@ def test_metric_arithmetic_reproduces_printed_summary():
                               (g["quant_fwd_us"], g["quant_fwd_tflops"], g["quant_fwd_gb_per_sec"], 1)]:
         assert bench.attn_tflops(s["B"], s["H"], s["Sq"], s["Skv"], s["D"], us * 1e-6, False) == pytest.approx(tfl, rel=1e-8)
         assert bench.pages_gbps(s["B"], s["H"], s["H"], s["Sq"], s["Skv"], s["D"], elt, us * 1e-6) == pytest.approx(gbs, rel=1e-6)
+
+
+@pytest.mark.parametrize("Sq,Skv,causal,wl,wr,sink", [
+    (9, 7, False, 2, 1, 0), (9, 7, True, 2, -1, 3), (20, 30, False, -1, -1, 0), (20, 30, True, -1, -1, 0),
+    (12, 12, False, 0, 0, 5), (15, 9, False, 3, 50, 2), (15, 9, True, 1, 0, 20), (40, 40, False, 5, 5, 9)])
+def test_local_flop_count_matches_enumeration(Sq, Skv, causal, wl, wr, sink):
+    """The kept-pair count behind the local-attention TFLOPS equals the oracle's own mask."""
+    import bench
+    q, k, v = np.zeros((1, 1, Sq, 1)), np.zeros((1, 1, Skv, 1)), np.ones((1, 1, Skv, 1))
+    _, L = attention_forward(q, k, v, 1.0, causal, window_left=wl, window_right=wr, sink=sink)
+    kept = np.where(np.isfinite(L), np.rint(np.exp(L)), 0).sum()   # all scores 0: LSE = ln(#kept)
+    assert bench.allowed_pairs(Sq, Skv, causal, wl, wr, sink) == int(kept)
 
 
 def test_nrms_definition_is_bf16_scale():
@@ -273,6 +373,14 @@ def _attention_pins_pass(fwd, merge):
                 return False
             if not np.array_equal(np.isinf(L), np.isinf(Lb)) or not np.allclose(L[np.isfinite(L)], Lb[np.isfinite(Lb)]):
                 return False
+        for causal, ks, wl, wr, sk in [(False, 0, 1, 2, 0), (True, 1, 2, 0, 1), (False, 0, 0, 0, 2)]:
+            O, L = fwd(q, k, v, 0.7, causal, ks, window_left=wl, window_right=wr, sink=sk)
+            Ob, Lb = attention_brute(q.tolist(), k.tolist(), v.tolist(), 0.7, causal, ks, wl, wr, sk)
+            Lb = np.array(Lb)
+            if not np.allclose(O, np.array(Ob), atol=1e-10):
+                return False
+            if not np.array_equal(np.isinf(L), np.isinf(Lb)) or not np.allclose(L[np.isfinite(L)], Lb[np.isfinite(Lb)]):
+                return False
         O, L = fwd(q, k, v, 0.6, True, 0)
         p1 = fwd(q, k[:, :, :2], v[:, :, :2], 0.6, True, 0)
         p2 = fwd(q, k[:, :, 2:], v[:, :, 2:], 0.6, True, 2)
@@ -296,6 +404,12 @@ FMT_FILE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "f
     ("m[live] + np.log(l)", "np.log(l)"),                                 # dropped max term
     ("w / np.where(finite, tot, 1.0)[None]", "w"),                        # unnormalised merge
     ("p = np.exp(s[live] - m[live, None])", "p = np.exp(s[live] + m[live, None])"),  # sign slip
+    ("key_pos[None, :] >= ridx[:, None] - int(window_left)",
+     "key_pos[None, :] > ridx[:, None] - int(window_left)"),             # off-by-one left edge
+    ("key_pos[None, :] <= ridx[:, None] + int(window_right)",
+     "key_pos[None, :] <= ridx[:, None] - int(window_right)"),           # mirrored right edge
+    ("(key_pos[None, :] < int(sink))", "(key_pos[None, :] <= int(sink))"),  # one sink key too many
+    ("in_win | (key_pos", "in_win & (key_pos"),                          # sink intersected, not joined
 ])
 def test_pins_catch_planted_mistakes(old, new):
     good = _load_mutant(ATT_FILE, "def merge_lse", "def merge_lse")
