@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the attention runs in the HIP
 kernels behind the C ABI declared in ``include/attn.h``. The functions
-``attn_fwd``, ``attn_fwd_chunk``, ``attn_fwd_splitkv``,
+``attn_fwd``, ``attn_fwd_chunk``, ``attn_fwd_window``, ``attn_fwd_splitkv``,
 ``attn_splitkv_workspace_bytes``, ``attn_splitkv_auto_splits``,
 ``attn_merge_lse2_host`` and ``attn_status_string`` carry the C names and
 arguments one for one (pointer arguments accept a torch tensor, a plain integer
@@ -20,7 +20,7 @@ import os
 
 __all__ = [
     "ATTN_BF16", "ATTN_FP8_E4M3FN", "STATUS", "AttnError", "lib", "library_path",
-    "attn_fwd", "attn_fwd_chunk", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
+    "attn_fwd", "attn_fwd_chunk", "attn_fwd_window", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
     "attn_splitkv_auto_splits", "attn_merge_lse2_host", "attn_status_string", "forward",
     "forward_splitkv", "merge_lse2_host",
 ]
@@ -32,7 +32,7 @@ STATUS = {
     5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_OVERFLOW", 7: "ATTN_ERR_SCALE", 8: "ATTN_ERR_HIP",
     9: "ATTN_ERR_WORKSPACE",
 }
-EXPORTED = ("attn_fwd", "attn_fwd_chunk", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
+EXPORTED = ("attn_fwd", "attn_fwd_chunk", "attn_fwd_window", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
             "attn_splitkv_auto_splits", "attn_merge_lse2_host", "attn_status_string")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +59,8 @@ def lib():
         L.attn_fwd.restype = i32
         L.attn_fwd_chunk.argtypes = fwd_args + [i64, vp]
         L.attn_fwd_chunk.restype = i32
+        L.attn_fwd_window.argtypes = fwd_args + [i64, i64, i64, i64, vp]
+        L.attn_fwd_window.restype = i32
         L.attn_fwd_splitkv.argtypes = fwd_args + [i64, vp, i64, vp]
         L.attn_fwd_splitkv.restype = i32
         L.attn_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
@@ -109,6 +111,15 @@ def attn_fwd_chunk(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dty
                                 _stream(stream))
 
 
+def attn_fwd_window(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype,
+                    q_descale=None, k_descale=None, v_descale=None, kv_start=0, window_left=-1,
+                    window_right=-1, sink=0, stream=0):
+    return lib().attn_fwd_window(_addr(q), _addr(k), _addr(v), _addr(out), _addr(lse), B, Hq, Hkv, Sq, Skv,
+                                 D, float(scale), int(bool(causal)), int(dtype),
+                                 _addr(q_descale), _addr(k_descale), _addr(v_descale), int(kv_start),
+                                 int(window_left), int(window_right), int(sink), _stream(stream))
+
+
 def attn_fwd_splitkv(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype,
                      q_descale=None, k_descale=None, v_descale=None, n_splits=0, workspace=None,
                      workspace_bytes=0, stream=0):
@@ -136,11 +147,12 @@ def attn_status_string(status):
 
 
 def forward(q, k, v, scale=None, causal=False, q_descale=None, k_descale=None, v_descale=None,
-            kv_start=0, out=None, lse=None, stream=None):
+            kv_start=0, out=None, lse=None, stream=None, window_left=-1, window_right=-1, sink=0):
     """(out, lse) for torch tensors q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] on the GPU.
 
     q/k/v are torch.bfloat16 or torch.float8_e4m3fn; descales are one-element
-    float32 device tensors or None.
+    float32 device tensors or None. A window side >= 0 or sink > 0 runs
+    ``attn_fwd_window``, else ``attn_fwd_chunk``.
     """
     import torch
     B, Hq, Sq, D = q.shape
@@ -160,6 +172,12 @@ def forward(q, k, v, scale=None, causal=False, q_descale=None, k_descale=None, v
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if window_left >= 0 or window_right >= 0 or sink > 0:
+        st = attn_fwd_window(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dt,
+                             q_descale, k_descale, v_descale, kv_start, window_left, window_right, sink, stream)
+        if st != 0:
+            raise AttnError(st, "attn_fwd_window")
+        return out, lse
     st = attn_fwd_chunk(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dt,
                         q_descale, k_descale, v_descale, kv_start, stream)
     if st != 0:

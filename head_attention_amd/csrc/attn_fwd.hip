@@ -43,6 +43,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <type_traits>
+#include <algorithm>
 
 #include "attn.h"
 
@@ -86,6 +87,10 @@ struct Params {
   int nsplit, split_len;
   float* o32;
   float* lse32;
+  // Local attention (instances with WIN): key position j (absolute, i.e.
+  // local key + kv_start) is allowed for query i iff i - wl <= j <= i + wr, or
+  // j < sink; causal additionally requires j <= i. Unbounded sides hold 2^30.
+  int wl, wr, sink;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -152,7 +157,7 @@ struct Tile {
   }
 };
 
-template <int D, bool CAUSAL, bool FP8>
+template <int D, bool CAUSAL, bool FP8, bool WIN>
 __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   using T = Tile<D, FP8>;
   constexpr int ROWB = T::ROWB;
@@ -204,6 +209,26 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   const int w_kv_end = CAUSAL ? min(Skv, max(0, min(qw + 32, p.Sq) - kv_start)) : Skv;
   const int w_ntiles = wave_live ? (w_kv_end + kBN - 1) / kBN : 0;
 
+  // The key tiles this workgroup loads, in order: u = 0 .. ntot-1 is tile
+  // tile_of(u). One run [0, ntiles) without a window; with one, up to two runs:
+  // the sink tiles from 0, then the tiles the rows' windows cover.
+  const int wl = p.wl, wr = p.wr, sink = p.sink;
+  int tA0 = 0, nA = ntiles, tB0 = 0, nB = 0;
+  if constexpr (WIN) {
+    const int q1 = rows_end;
+    const int cap = CAUSAL ? q1 - 1 : 0x7fffffff;                 // last key position any row may see
+    const int wlo = q0 - wl <= kv_start ? 0 : q0 - wl - kv_start;
+    const int whi = min(Skv - 1, min(q1 - 1 + wr, cap) - kv_start);
+    const int shi = min(Skv - 1, min(sink - 1, cap) - kv_start);
+    const int b0 = wlo / kBN, b1 = whi >= wlo ? whi / kBN + 1 : b0;  // window tiles [b0, b1)
+    const int a1 = shi >= 0 ? shi / kBN + 1 : 0;                      // sink tiles [0, a1)
+    if (a1 == 0) { tA0 = b0; nA = b1 - b0; }
+    else if (b1 > b0 && b0 <= a1) { tA0 = 0; nA = max(a1, b1); }
+    else { tA0 = 0; nA = a1; tB0 = b0; nB = b1 - b0; }
+  }
+  const int ntot = nA + nB;
+  auto tile_of = [&](int u) __attribute__((always_inline)) { return u < nA ? tA0 + u : tB0 + (u - nA); };
+
   // Q fragments (B operand of S^T = K Q^T); rows >= Sq read as zero.
   bf16x8 qf16[FP8 ? 1 : D / 16];
   i32x8 qf8[FP8 ? D / 64 : 1];
@@ -239,9 +264,9 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   constexpr int PW = 2 * T::NINSTR / kWaves;   // pieces per wave per tile
   static_assert(PW >= 1 && PW * kWaves == 2 * T::NINSTR, "tile pieces must split evenly over waves");
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  auto issue = [&](int t) {
-    const int key0 = t * kBN;
-    const int slot = t % kStages;
+  auto issue = [&](int u) __attribute__((always_inline)) {
+    const int key0 = tile_of(u) * kBN;
+    const int slot = u % kStages;
 #pragma unroll
     for (int j = 0; j < PW; ++j) {
       const int ins = wv * PW + j;
@@ -275,19 +300,23 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   // is refilled with tile t + kStages - 1.
 #pragma unroll
   for (int u = 0; u < kStages - 1; ++u)
-    if (u < ntiles) issue(u);
-  // One iteration per key tile. Tiles from first_masked on take the element
-  // mask (keys past Skv, or causal keys after the wave's first row); the
-  // others are compiled without it, so no mask work is ever speculated.
-  auto step = [&](int t, auto masked_c) __attribute__((always_inline)) {
-    if (t + 2 < ntiles) wait_vmcnt<2 * PW>();
-    else if (t + 1 < ntiles) wait_vmcnt<PW>();
+    if (u < ntot) issue(u);
+  // Tile u of the sequence: wait for this wave's copies of it, barrier, queue
+  // tile u + kStages - 1 into the slot every wave is done with.
+  auto sync = [&](int u) __attribute__((always_inline)) {
+    if (u + 2 < ntot) wait_vmcnt<2 * PW>();
+    else if (u + 1 < ntot) wait_vmcnt<PW>();
     else wait_vmcnt<0>();
     __syncthreads();
-    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
-    if (t >= w_ntiles) return;
-    const LDS_AS char* ks = smem + ((t % kStages) * 2 + 0) * T::BYTES;
-    const LDS_AS char* vs = smem + ((t % kStages) * 2 + 1) * T::BYTES;
+    if (u + kStages - 1 < ntot) issue(u + kStages - 1);
+  };
+  // The tile's scores, softmax and P V for this wave. Masked tiles take the
+  // element mask; the others are compiled without it, so no mask work is ever
+  // speculated on them.
+  auto step = [&](int u, auto masked_c) __attribute__((always_inline)) {
+    const int t = tile_of(u);
+    const LDS_AS char* ks = smem + ((u % kStages) * 2 + 0) * T::BYTES;
+    const LDS_AS char* vs = smem + ((u % kStages) * 2 + 1) * T::BYTES;
 
     // ---- S^T = K Q^T ----
     f32x16 s[NKB];
@@ -323,7 +352,9 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-          const bool ok = key < Skv && (!CAUSAL || key + kv_start <= qi);
+          const int kp = key + kv_start;
+          bool ok = key < Skv && (!CAUSAL || kp <= qi);
+          if constexpr (WIN) ok = ok && ((kp >= qi - wl && kp <= qi + wr) || kp < sink);
           s[kb][i] = ok ? s[kb][i] : -INFINITY;
         }
     }
@@ -429,10 +460,35 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
       }
     }
   };
-  const int first_masked = CAUSAL ? min(Skv / kBN, max(0, qw - kv_start + 1) / kBN) : Skv / kBN;
-  int t = 0;
-  for (; t < min(first_masked, ntiles); ++t) step(t, std::false_type{});
-  for (; t < ntiles; ++t) step(t, std::true_type{});
+  if constexpr (!WIN) {
+    const int first_masked = CAUSAL ? min(Skv / kBN, max(0, qw - kv_start + 1) / kBN) : Skv / kBN;
+    int u = 0;
+    for (; u < min(first_masked, ntot); ++u) {
+      sync(u);
+      if (u < w_ntiles) step(u, std::false_type{});
+    }
+    for (; u < ntot; ++u) {
+      sync(u);
+      if (u < w_ntiles) step(u, std::true_type{});
+    }
+  } else {
+    // Per tile and wave: skip it (no key of it is allowed for any of the
+    // wave's rows), take it whole, or mask it.
+    const int r_lo = qw, r_hi = min(qw + 31, p.Sq - 1);
+    const int cap = CAUSAL ? r_hi : 0x7fffffff;
+    for (int u = 0; u < ntot; ++u) {
+      sync(u);
+      if (!wave_live) continue;
+      const int t = tile_of(u);
+      const int k_lo = t * kBN + kv_start, k_hi = k_lo + kBN - 1;
+      const bool any = t * kBN < Skv && ((k_hi >= r_lo - wl && k_lo <= min(r_hi + wr, cap)) || (k_lo < sink && k_lo <= cap));
+      if (!any) continue;
+      const bool whole = t * kBN + kBN <= Skv && (!CAUSAL || k_hi <= r_lo) &&
+                         ((k_lo >= r_hi - wl && k_hi <= r_lo + wr) || k_hi < sink);
+      if (whole) step(u, std::false_type{});
+      else step(u, std::true_type{});
+    }
+  }
 
 
   // ---- epilogue: O = O_acc * oscale / l (bf16), LSE = ln2 * (m + log2 l) ----
@@ -523,8 +579,9 @@ __global__ void __launch_bounds__(256) merge_splits_kernel(const float* __restri
 typedef void (*kernel_fn)(Params);
 
 template <int D, bool FP8>
-kernel_fn pick(bool causal) {
-  return causal ? attn_fwd_kernel<D, true, FP8> : attn_fwd_kernel<D, false, FP8>;
+kernel_fn pick(bool causal, bool win) {
+  if (win) return causal ? attn_fwd_kernel<D, true, FP8, true> : attn_fwd_kernel<D, false, FP8, true>;
+  return causal ? attn_fwd_kernel<D, true, FP8, false> : attn_fwd_kernel<D, false, FP8, false>;
 }
 
 }  // namespace hat
@@ -541,10 +598,12 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
                             float scale, int causal, attn_dtype_t dtype,
                             const float* qd, const float* kd, const float* vd, int64_t kv_start,
-                            int64_t nsplit, void* workspace, int64_t workspace_bytes, void* stream) {
+                            int64_t nsplit, void* workspace, int64_t workspace_bytes, void* stream,
+                            int64_t window_left = -1, int64_t window_right = -1, int64_t sink = 0) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3FN) return ATTN_ERR_DTYPE;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || kv_start < 0) return ATTN_ERR_SHAPE;
+  if (window_left < -1 || window_right < -1 || sink < 0) return ATTN_ERR_SHAPE;
   if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return ATTN_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
   const int64_t elt = dtype == ATTN_BF16 ? 2 : 1;
@@ -558,7 +617,10 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
   // Per-head slices are addressed with 32-bit offsets (plus one tile of slack).
   const int64_t lim = (int64_t)1 << 31;
-  if ((Sq + kBM) * D * 2 >= lim || (Skv + kBN) * rowb >= lim || Sq + kBM >= lim || kv_start >= lim) return ATTN_ERR_OVERFLOW;
+  if ((Sq + kBM) * D * 2 >= lim || (Skv + kBN) * rowb >= lim || Sq + kBM >= lim) return ATTN_ERR_OVERFLOW;
+  // Key positions stay below 2^30, so position arithmetic (with the unbounded
+  // window sides held as 2^30) never leaves int range.
+  if (kv_start + Skv + kBN >= ((int64_t)1 << 30)) return ATTN_ERR_OVERFLOW;
   const int64_t n_qtiles = (Sq + kBM - 1) / kBM;
   if (nsplit < 1 || nsplit > kMaxSplits) return ATTN_ERR_SHAPE;
   // Key splits are whole tiles; fewer tiles than splits leaves fewer splits.
@@ -597,10 +659,15 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   p.split_len = nsp > 1 ? (int)(per * kBN) : (int)Skv;
   p.o32 = nsp > 1 ? (float*)workspace : nullptr;
   p.lse32 = nsp > 1 ? (float*)workspace + nsp * rows * D : nullptr;
+  constexpr int64_t kUnbounded = (int64_t)1 << 30;
+  const bool win = window_left >= 0 || window_right >= 0 || sink > 0;
+  p.wl = (int)(window_left < 0 ? kUnbounded : std::min(window_left, kUnbounded));
+  p.wr = (int)(window_right < 0 ? kUnbounded : std::min(window_right, kUnbounded));
+  p.sink = (int)std::min(sink, kUnbounded);
 
   kernel_fn fn;
-  if (dtype == ATTN_BF16) fn = D == 128 ? pick<128, false>(causal) : pick<64, false>(causal);
-  else fn = D == 128 ? pick<128, true>(causal) : pick<64, true>(causal);
+  if (dtype == ATTN_BF16) fn = D == 128 ? pick<128, false>(causal, win) : pick<64, false>(causal, win);
+  else fn = D == 128 ? pick<128, true>(causal, win) : pick<64, true>(causal, win);
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   if (nsp > 1) {
@@ -653,6 +720,16 @@ extern "C" attn_status_t attn_fwd_chunk(const void* q, const void* k, const void
                                         const float* v_descale, int64_t kv_start, void* stream) {
   return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, q_descale, k_descale,
                 v_descale, kv_start, 1, nullptr, 0, stream);
+}
+
+extern "C" attn_status_t attn_fwd_window(const void* q, const void* k, const void* v, void* out, float* lse,
+                                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                                         float scale, int causal, attn_dtype_t dtype,
+                                         const float* q_descale, const float* k_descale, const float* v_descale,
+                                         int64_t kv_start, int64_t window_left, int64_t window_right, int64_t sink,
+                                         void* stream) {
+  return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, q_descale, k_descale,
+                v_descale, kv_start, 1, nullptr, 0, stream, window_left, window_right, sink);
 }
 
 extern "C" int64_t attn_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int64_t D) {

@@ -52,11 +52,13 @@ typedef enum {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,      /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = 2,     /* a negative size, Hkv = 0 with Hq > 0, Hq % Hkv != 0, kv_start < 0, n_splits outside 0..256 */
+  ATTN_ERR_SHAPE = 2,     /* a negative size, Hkv = 0 with Hq > 0, Hq % Hkv != 0, kv_start < 0,
+                             n_splits outside 0..256, a window side < -1 or sink < 0 */
   ATTN_ERR_HEAD_DIM = 3,  /* D is not 64 or 128 */
   ATTN_ERR_DTYPE = 4,     /* unknown attn_dtype_t */
   ATTN_ERR_ALIGN = 5,     /* q, k, v or out not 16-byte aligned, or lse not 4-byte aligned */
-  ATTN_ERR_OVERFLOW = 6,  /* one head's slice reaches 2^31 bytes, or the grid is too large */
+  ATTN_ERR_OVERFLOW = 6,  /* one head's slice reaches 2^31 bytes, kv_start + Skv reaches 2^30,
+                             or the grid is too large */
   ATTN_ERR_SCALE = 7,     /* scale is not finite or not > 0 */
   ATTN_ERR_HIP = 8,       /* the kernel launch failed */
   ATTN_ERR_WORKSPACE = 9  /* attn_fwd_splitkv: workspace NULL, not 16-byte aligned, or too small */
@@ -100,6 +102,27 @@ attn_status_t attn_fwd_chunk(const void* q, const void* k, const void* v, void* 
                              float scale, int causal, attn_dtype_t dtype,
                              const float* q_descale, const float* k_descale, const float* v_descale,
                              int64_t kv_start, void* stream);
+
+/*
+ * attn_fwd_window — attn_fwd_chunk with local (sliding-window) attention and
+ * attention sinks, the window_size_left / window_size_right arguments of the
+ * fmha_v3_fwd call on the page "F8 fmha ASM gfx950" (Test Result section) and
+ * the window / sink configurations of the page "[Proposal] ROCm (AMD
+ * Instinct) support for the core attention and distributed init". With key
+ * position j = (key index + kv_start), key j is allowed for query i iff
+ *     (window_left < 0  or j >= i - window_left) and
+ *     (window_right < 0 or j <= i + window_right),  or  j < sink,
+ * and, with causal, also j <= i. window_left / window_right = -1 means that
+ * side is unbounded; sink = 0 means no sink keys. All -1, -1, 0 is
+ * attn_fwd_chunk. Key tiles no row of a workgroup can see are not read.
+ * Errors as attn_fwd_chunk; ATTN_ERR_SHAPE for window sides < -1 or sink < 0.
+ */
+attn_status_t attn_fwd_window(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                              float scale, int causal, attn_dtype_t dtype,
+                              const float* q_descale, const float* k_descale, const float* v_descale,
+                              int64_t kv_start, int64_t window_left, int64_t window_right, int64_t sink,
+                              void* stream);
 
 /*
  * attn_merge_lse2_host — merge two partial results on the HOST.

@@ -69,6 +69,8 @@ P = 1 << 20
     (dict(lse=P + 2), 5),
     (dict(Sq=1 << 30), 6),
     (dict(Skv=1 << 30), 6),
+    (dict(kv_start=(1 << 30) - 100), 6),     # key positions must stay below 2^30
+    (dict(kv_start=(1 << 30) - 65, Skv=1), 6),    # kv_start + Skv + one key tile = 2^30
 ])
 def test_fail_closed_validation(L, args, status):
     a = dict(q=P, k=P, v=P, out=P, lse=P, B=1, Hq=4, Hkv=2, Sq=100, Skv=100, D=128, scale=0.1,
@@ -96,6 +98,23 @@ def test_splitkv_fail_closed_validation(L, args, status):
     st = ha.attn_fwd_splitkv(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
                              a["Skv"], a["D"], 0.1, 0, 0, None, None, None, a["n_splits"], a["workspace"],
                              a["wbytes"], 0)
+    assert st == status, (args, ha.STATUS.get(st, st))
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(wl=-2), 2),
+    (dict(wr=-5), 2),
+    (dict(sink=-1), 2),
+    (dict(wl=3, D=96), 3),
+    (dict(wl=3, q=None), 1),
+    (dict(wl=3, kv_start=-1), 2),
+    (dict(wl=3, kv_start=1 << 30), 6),
+])
+def test_window_fail_closed_validation(L, args, status):
+    a = dict(q=P, k=P, v=P, out=P, lse=P, D=128, kv_start=0, wl=-1, wr=-1, sink=0)
+    a.update(args)
+    st = ha.attn_fwd_window(a["q"], a["k"], a["v"], a["out"], a["lse"], 1, 4, 2, 100, 100, a["D"], 0.1, 0, 0,
+                            None, None, None, a["kv_start"], a["wl"], a["wr"], a["sink"], 0)
     assert st == status, (args, ha.STATUS.get(st, st))
 
 
