@@ -14,6 +14,8 @@ Contents
 ``attention``  the plain fp64 forward: dequantise, GQA head map, scores,
                causal mask with a key offset, softmax normalisation, output and
                natural-log LSE; plus the merge of partial (O, LSE) results.
+``backward``   the plain fp64 backward (dQ, dK, dV) by the chain rule on the
+               same forward definition, with P recomputed from Q and K.
 ``brute``      a pure-Python nested-loop version for tiny shapes, computed by a
                different route (no max subtraction, ``math.fsum``), used only to
                pin the numpy version.
@@ -25,3 +27,4 @@ routines, the pages' printed figures). No function here is "parity unpinned".
 
 from .formats import decode_bf16, decode_e4m3fn, dequantise  # noqa: F401
 from .attention import attention_forward, merge_lse  # noqa: F401
+from .backward import attention_backward  # noqa: F401
