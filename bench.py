@@ -201,6 +201,63 @@ def bench_workload(args, w, make_inputs):
         "workgroups": w.B * w.Hq * ((w.Sq + 255) // 256)}), flush=True)
 
 
+def bench_backward(args, w):
+    """Time attn_bwd (dQ, dK, dV) on one workload; prints one JSON line. The
+    forward (O, LSE) is computed once before the timed region; each step is one
+    attn_bwd call (its dQ, dK/dV and, where used, group-sum kernels)."""
+    import numpy as np
+    import torch
+    import head_attention_amd as ha
+    from synth import normal, to_bf16_bits
+    dev = torch.device("cuda:0")
+    base = 1000 * w.wid
+
+    def put(seed, shape):
+        a = to_bf16_bits(normal(shape, seed))
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    Q = put(base + 0, (w.B, w.Hq, w.Sq, w.D))
+    K = put(base + 1, (w.B, w.Hkv, w.Skv, w.D))
+    V = put(base + 2, (w.B, w.Hkv, w.Skv, w.D))
+    dO = put(base + 3, (w.B, w.Hq, w.Sq, w.D))
+    causal = bool(w.causal[-1])
+    O, L = ha.forward(Q, K, V, scale=w.scale, causal=causal)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    need = ha.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        st = ha.attn_bwd(Q, K, V, O, dO, L, dQ, dK, dV, w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.scale, int(causal),
+                         ha.ATTN_BF16, ws, need, stream.cuda_stream)
+        if st != 0:
+            raise ha.AttnError(st, "attn_bwd")
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        launch()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tl = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+    flops = 2.5 * attn_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, causal)   # five products of 2*D flops per pair
+    tf = flops / tl.mean() / 1e12
+    print(json.dumps({
+        "metric": f"attn bwd TFLOPS (bf16) at {w.name}", "value": round(tf, 2), "unit": "TFLOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: backward B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Skv{w.Skv} D{w.D} "
+                               f"{'causal' if causal else 'non-causal'}, deterministic",
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "causal": causal},
+        "ms_mean": round(float(tl.mean()) * 1e3, 4), "ms_p50": round(float(np.median(tl)) * 1e3, 4),
+        "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "workspace_bytes": need}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +295,8 @@ def main():
     from synth import WORKLOADS, make_inputs
 
     if args.workload:
+        if args.workload.startswith("bwd"):
+            return bench_backward(args, WORKLOADS[args.workload])
         return bench_workload(args, WORKLOADS[args.workload], make_inputs)
 
     dev = torch.device("cuda:0")

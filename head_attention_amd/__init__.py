@@ -1,15 +1,16 @@
-"""Python binding of the gfx950 fused attention forward (``libattn.so``).
+"""Python binding of the gfx950 fused attention forward and backward (``libattn.so``).
 
 Argument marshalling only: every step of the attention runs in the HIP
 kernels behind the C ABI declared in ``include/attn.h``. The functions
 ``attn_fwd``, ``attn_fwd_chunk``, ``attn_fwd_window``, ``attn_fwd_splitkv``,
 ``attn_splitkv_workspace_bytes``, ``attn_splitkv_auto_splits``,
-``attn_merge_lse2_host`` and ``attn_status_string`` carry the C names and
+``attn_bwd``, ``attn_bwd_workspace_bytes``, ``attn_merge_lse2_host`` and
+``attn_status_string`` carry the C names and
 arguments one for one (pointer arguments accept a torch tensor, a plain integer
 address or None) and return what the C function returns. ``forward`` and
 ``forward_splitkv`` are convenience wrappers that read the sizes off torch
 tensors, allocate the outputs (and the split workspace) with torch and raise
-``AttnError`` on a non-OK status.
+``AttnError`` on a non-OK status; ``backward`` does the same for ``attn_bwd``.
 
 There is no fallback: if the library is missing, loading raises.
 """
@@ -22,7 +23,7 @@ __all__ = [
     "ATTN_BF16", "ATTN_FP8_E4M3FN", "STATUS", "AttnError", "lib", "library_path",
     "attn_fwd", "attn_fwd_chunk", "attn_fwd_window", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
     "attn_splitkv_auto_splits", "attn_merge_lse2_host", "attn_status_string", "forward",
-    "forward_splitkv", "merge_lse2_host",
+    "forward_splitkv", "merge_lse2_host", "attn_bwd", "attn_bwd_workspace_bytes", "backward",
 ]
 
 ATTN_BF16 = 0
@@ -33,7 +34,8 @@ STATUS = {
     9: "ATTN_ERR_WORKSPACE",
 }
 EXPORTED = ("attn_fwd", "attn_fwd_chunk", "attn_fwd_window", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
-            "attn_splitkv_auto_splits", "attn_merge_lse2_host", "attn_status_string")
+            "attn_splitkv_auto_splits", "attn_merge_lse2_host", "attn_status_string", "attn_bwd",
+            "attn_bwd_workspace_bytes")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libattn.so")
@@ -69,6 +71,10 @@ def lib():
         L.attn_splitkv_auto_splits.restype = i64
         L.attn_merge_lse2_host.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64]
         L.attn_merge_lse2_host.restype = i32
+        L.attn_bwd.argtypes = [vp] * 9 + [i64] * 6 + [f32, i32, i32, vp, i64, vp]
+        L.attn_bwd.restype = i32
+        L.attn_bwd_workspace_bytes.argtypes = [i64] * 6
+        L.attn_bwd_workspace_bytes.restype = i64
         L.attn_status_string.argtypes = [i32]
         L.attn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -221,6 +227,47 @@ def forward_splitkv(q, k, v, n_splits=0, scale=None, causal=False, q_descale=Non
     if st != 0:
         raise AttnError(st, "attn_fwd_splitkv")
     return out, lse
+
+
+def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype,
+             workspace, workspace_bytes, stream=0):
+    return lib().attn_bwd(_addr(q), _addr(k), _addr(v), _addr(out), _addr(dout), _addr(lse), _addr(dq),
+                          _addr(dk), _addr(dv), B, Hq, Hkv, Sq, Skv, D, float(scale), int(bool(causal)),
+                          int(dtype), _addr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D):
+    return lib().attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D)
+
+
+def backward(q, k, v, out, dout, lse, scale=None, causal=False, workspace=None, stream=None):
+    """(dq, dk, dv) for bf16 GPU tensors q/out/dout [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] and
+    lse [B,Hq,Sq] fp32 from ``forward``. The workspace (a uint8 GPU tensor) is
+    allocated with torch unless one is passed."""
+    import torch
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    for t in (q, k, v, out, dout):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("q, k, v, out, dout must be contiguous bf16 GPU tensors")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    need = attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D)
+    if need < 0:
+        raise AttnError(2, "attn_bwd_workspace_bytes")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, ATTN_BF16,
+                  workspace, wbytes, stream)
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
 
 
 def merge_lse2_host(o1, lse1, o2, lse2):

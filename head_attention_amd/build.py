@@ -11,7 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = [os.path.join(HERE, "csrc", "attn_fwd.hip"), os.path.join(HERE, "csrc", "merge_host.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", "attn_fwd.hip"), os.path.join(HERE, "csrc", "attn_bwd.hip"),
+           os.path.join(HERE, "csrc", "merge_host.cpp")]
 
 # Packed fp32 VALU forms are disabled for every HIP translation unit.
 HIPCC_FLAGS = [

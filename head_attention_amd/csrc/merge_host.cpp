@@ -72,7 +72,7 @@ extern "C" const char* attn_status_string(attn_status_t s) {
     case ATTN_ERR_OVERFLOW: return "ATTN_ERR_OVERFLOW: a head slice or the grid exceeds 32-bit addressing";
     case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE: scale must be finite and > 0";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: kernel launch failed";
-    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: split-KV workspace missing, misaligned or too small";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing, misaligned or too small";
   }
   return "ATTN_ERR_UNKNOWN";
 }

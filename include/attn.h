@@ -61,7 +61,7 @@ typedef enum {
                              or the grid is too large */
   ATTN_ERR_SCALE = 7,     /* scale is not finite or not > 0 */
   ATTN_ERR_HIP = 8,       /* the kernel launch failed */
-  ATTN_ERR_WORKSPACE = 9  /* attn_fwd_splitkv: workspace NULL, not 16-byte aligned, or too small */
+  ATTN_ERR_WORKSPACE = 9  /* attn_fwd_splitkv / attn_bwd: workspace NULL, misaligned, or too small */
 } attn_status_t;
 
 /*
@@ -180,6 +180,44 @@ int64_t attn_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t 
  * splits (each at least 16 key tiles, at most 16) that reach 90 %, or 1 if
  * none does. -1 on invalid arguments. Queries the current HIP device. */
 int64_t attn_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int64_t D);
+
+/*
+ * attn_bwd — gradients of the attention forward (bf16): dQ, dK, dV, the
+ * tensors the page "feat(attention): add strict bitwise ROCm path" checks next
+ * to out and lse (Latest status) and whose deterministic backward it times
+ * (section "What the strict contract costs"). With P the forward's softmax
+ * (recomputed from q, k and lse) and D_i = sum_d dout[i,d] * out[i,d]:
+ *     dv = P^T dout,   dS = P * (dout v^T - D),
+ *     dq = scale * dS k,   dk = scale * dS^T q,
+ * summed over the query heads of each KV head for dk and dv.
+ *
+ *   q, out, dout, dq  [B, Hq, Sq, D] bf16 (out and lse as attn_fwd returned
+ *                     them for the same q, k, v, scale and causal)
+ *   k, v, dk, dv      [B, Hkv, Skv, D] bf16
+ *   lse               [B, Hq, Sq] fp32 (natural log, scale included)
+ *   causal            top-left: key j is allowed for query i iff j <= i
+ *   dtype             ATTN_BF16 only (ATTN_ERR_DTYPE otherwise)
+ *   workspace         device buffer of at least attn_bwd_workspace_bytes(...)
+ *                     bytes, 256-byte aligned, owned by the caller; its
+ *                     contents on entry do not matter. It may be NULL when
+ *                     that size is 0.
+ * dq, dk, dv are written in full (zeros where nothing contributes); rows with
+ * lse = -inf contribute nothing. The result is deterministic: no atomics,
+ * every sum in a fixed order, so identical inputs give identical bits, and a
+ * batch entry's gradients do not depend on the other entries. Two calls that
+ * overlap in time must not share a workspace. Errors as attn_fwd;
+ * ATTN_ERR_WORKSPACE when the workspace is missing, misaligned or too small.
+ */
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                       float scale, int causal, attn_dtype_t dtype,
+                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_bwd needs: 8 per query row (its LSE and D), plus
+ * fp32 partial dK and dV per query head (8 * B * Hq * Skv * D) when grouped KV
+ * heads are split over workgroups; -1 on invalid arguments. */
+int64_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_status_string(attn_status_t s);

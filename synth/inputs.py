@@ -29,6 +29,12 @@ pages' Qwen3-8B validation, 16384 tokens, a 4096-token sliding window
 (window_left 4095) and 4 sink tokens; and "video_band", the video-DiT shape
 (75600 tokens = 21 frames of 3600) with a band of three frames on either side
 (window 10800 / 10800) and the first frame as sinks (3600).
+
+The backward is timed on "bwd_llm": B1, 32/8 heads, S4096, D128, causal, the
+largest sequence length of the deterministic-backward table on the page
+"feat(attention): add strict bitwise ROCm path" (section "What the strict
+contract costs"), with that page's Qwen3-8B head layout; dO is a fourth
+N(0, 1) draw (seed base + 3).
 """
 
 from dataclasses import dataclass, field
@@ -91,6 +97,9 @@ WORKLOADS = {
         Workload(11, "video_band", 1, 5, 5, 75600, 75600, 128, "bf16", (False,),
                  note="video-DiT shape with a +/-3-frame band and the first frame as sinks",
                  window_left=10800, window_right=10800, sink=3600),
+        # the backward's timed shape
+        Workload(12, "bwd_llm", 1, 32, 8, 4096, 4096, 128, "bf16", (True,),
+                 note="attention backward, B1, 32 query / 8 KV heads, S4096, D128, causal"),
     ]
 }
 

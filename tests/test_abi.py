@@ -118,6 +118,45 @@ def test_window_fail_closed_validation(L, args, status):
     assert st == status, (args, ha.STATUS.get(st, st))
 
 
+@pytest.mark.parametrize("args,status", [
+    (dict(dtype=1), 4),
+    (dict(D=96), 3),
+    (dict(Hq=3), 2),
+    (dict(Sq=-1), 2),
+    (dict(scale=0.0), 7),
+    (dict(dq=None), 1),
+    (dict(dk=None), 1),
+    (dict(lse=None), 1),
+    (dict(dout=P + 8), 5),
+    (dict(dv=P + 4), 5),
+    (dict(workspace=None), 9),
+    (dict(workspace=P + 16), 9),
+    (dict(wbytes=10), 9),
+    (dict(Skv=1 << 30), 6),
+])
+def test_backward_fail_closed_validation(L, args, status):
+    a = dict(q=P, k=P, v=P, out=P, dout=P, lse=P, dq=P, dk=P, dv=P, Hq=4, Sq=100, D=128, scale=0.1,
+             dtype=0, workspace=P, wbytes=1 << 40, Skv=100)
+    a.update(args)
+    st = ha.attn_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                     1, a["Hq"], 2, a["Sq"], a["Skv"], a["D"], a["scale"], 1, a["dtype"], a["workspace"],
+                     a["wbytes"], 0)
+    assert st == status, (args, ha.STATUS.get(st, st))
+
+
+def test_backward_workspace_size():
+    # 8 bytes of row statistics per query row, padded to 256 bytes ...
+    assert ha.attn_bwd_workspace_bytes(1, 2, 2, 100, 100, 128) == 1792
+    assert ha.attn_bwd_workspace_bytes(2, 3, 3, 64, 999, 64) == 2 * 3 * 64 * 8
+    # ... plus fp32 partial dK and dV per query head when a KV head's group is
+    # split over workgroups (few KV-head key blocks) ...
+    assert ha.attn_bwd_workspace_bytes(1, 32, 8, 4096, 4096, 128) == 32 * 4096 * 8 + 2 * 32 * 4096 * 128 * 4
+    # ... but not when the group is summed in registers (enough blocks to fill the chip)
+    assert ha.attn_bwd_workspace_bytes(64, 4, 2, 64, 1024, 128) == 64 * 4 * 64 * 8
+    assert ha.attn_bwd_workspace_bytes(1, 4, 3, 10, 10, 128) == -1
+    assert ha.attn_bwd_workspace_bytes(1, 4, 2, 10, 10, 96) == -1
+
+
 def test_splitkv_workspace_size():
     assert ha.attn_splitkv_workspace_bytes(2, 3, 100, 128, 1) == 0
     assert ha.attn_splitkv_workspace_bytes(2, 3, 100, 128, 4) == 4 * 2 * 3 * 100 * 129 * 4
