@@ -78,11 +78,11 @@ def measured_traffic():
     """
     import hashlib
     prof = os.path.join(ROOT, "profiles", "attn_fwd_kernel_video_dit_B1H5S75600D128_hbm_traffic.md")
-    src = os.path.join(ROOT, "head_attention_amd", "csrc", "attn_fwd.hip")
+    srcs = [os.path.join(ROOT, "head_attention_amd", "csrc", f) for f in ("attn_fwd.hip", "device_common.h")]
     try:
         line = [l for l in open(prof) if l.startswith("traffic_json: ")][0]
         rec = json.loads(line[len("traffic_json: "):])
-        if rec["source_sha256"] != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        if rec["source_sha256"] != hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest():
             return {}
         return rec["bytes_per_launch"]
     except (OSError, IndexError, KeyError, ValueError):
