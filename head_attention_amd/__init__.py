@@ -4,7 +4,7 @@ Argument marshalling only: every step of the attention runs in the HIP
 kernels behind the C ABI declared in ``include/attn.h``. The functions
 ``attn_fwd``, ``attn_fwd_chunk``, ``attn_fwd_window``, ``attn_fwd_splitkv``,
 ``attn_splitkv_workspace_bytes``, ``attn_splitkv_auto_splits``,
-``attn_bwd``, ``attn_bwd_workspace_bytes``, ``attn_merge_lse2_host`` and
+``attn_bwd``, ``attn_bwd_chunk``, ``attn_bwd_workspace_bytes``, ``attn_merge_lse2_host`` and
 ``attn_status_string`` carry the C names and
 arguments one for one (pointer arguments accept a torch tensor, a plain integer
 address or None) and return what the C function returns. ``forward`` and
@@ -23,7 +23,7 @@ __all__ = [
     "ATTN_BF16", "ATTN_FP8_E4M3FN", "STATUS", "AttnError", "lib", "library_path",
     "attn_fwd", "attn_fwd_chunk", "attn_fwd_window", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
     "attn_splitkv_auto_splits", "attn_merge_lse2_host", "attn_status_string", "forward",
-    "forward_splitkv", "merge_lse2_host", "attn_bwd", "attn_bwd_workspace_bytes", "backward",
+    "forward_splitkv", "merge_lse2_host", "attn_bwd", "attn_bwd_chunk", "attn_bwd_workspace_bytes", "backward",
 ]
 
 ATTN_BF16 = 0
@@ -35,7 +35,7 @@ STATUS = {
 }
 EXPORTED = ("attn_fwd", "attn_fwd_chunk", "attn_fwd_window", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
             "attn_splitkv_auto_splits", "attn_merge_lse2_host", "attn_status_string", "attn_bwd",
-            "attn_bwd_workspace_bytes")
+            "attn_bwd_chunk", "attn_bwd_workspace_bytes")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libattn.so")
@@ -73,6 +73,8 @@ def lib():
         L.attn_merge_lse2_host.restype = i32
         L.attn_bwd.argtypes = [vp] * 9 + [i64] * 6 + [f32, i32, i32, vp, i64, vp]
         L.attn_bwd.restype = i32
+        L.attn_bwd_chunk.argtypes = [vp] * 9 + [i64] * 6 + [f32, i32, i32, i64, vp, i64, vp]
+        L.attn_bwd_chunk.restype = i32
         L.attn_bwd_workspace_bytes.argtypes = [i64] * 6
         L.attn_bwd_workspace_bytes.restype = i64
         L.attn_status_string.argtypes = [i32]
@@ -236,14 +238,22 @@ def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale,
                           int(dtype), _addr(workspace), int(workspace_bytes), _stream(stream))
 
 
+def attn_bwd_chunk(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, kv_start,
+                   workspace, workspace_bytes, stream=0):
+    return lib().attn_bwd_chunk(_addr(q), _addr(k), _addr(v), _addr(out), _addr(dout), _addr(lse), _addr(dq),
+                                _addr(dk), _addr(dv), B, Hq, Hkv, Sq, Skv, D, float(scale), int(bool(causal)),
+                                int(dtype), int(kv_start), _addr(workspace), int(workspace_bytes), _stream(stream))
+
+
 def attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D):
     return lib().attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D)
 
 
-def backward(q, k, v, out, dout, lse, scale=None, causal=False, workspace=None, stream=None):
+def backward(q, k, v, out, dout, lse, scale=None, causal=False, workspace=None, stream=None, kv_start=0):
     """(dq, dk, dv) for bf16 GPU tensors q/out/dout [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] and
     lse [B,Hq,Sq] fp32 from ``forward``. The workspace (a uint8 GPU tensor) is
-    allocated with torch unless one is passed."""
+    allocated with torch unless one is passed. kv_start > 0 runs ``attn_bwd_chunk``
+    (out and lse then belong to the attention over all keys)."""
     import torch
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
@@ -263,10 +273,10 @@ def backward(q, k, v, out, dout, lse, scale=None, causal=False, workspace=None, 
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, ATTN_BF16,
-                  workspace, wbytes, stream)
+    st = attn_bwd_chunk(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, ATTN_BF16,
+                        kv_start, workspace, wbytes, stream)
     if st != 0:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, "attn_bwd_chunk")
     return dq, dk, dv
 
 

@@ -67,6 +67,7 @@ struct Params {
   float* dk32;    // per-query-head fp32 partials [B, Hq, Skv, D] (null: write dk/dv directly)
   float* dv32;
   int B, Hq, Hkv, Sq, Skv, group, hpw, n_qtiles, n_kblocks;
+  int kv_start;   // key j sits at position j + kv_start (causal: allowed for query i iff j + kv_start <= i)
   float c;        // scale * log2(e)
   float scale;
 };
@@ -160,7 +161,7 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dq_kernel(const Params p) {
   const int b = bh / p.Hq, h = bh % p.Hq, hk = h / p.group;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, n = lane & 31;
-  const int Sq = p.Sq, Skv = p.Skv;
+  const int Sq = p.Sq, Skv = p.Skv, kv_start = p.kv_start;
   const float c = p.c, scale = p.scale;   // locals: lambdas must not capture the kernel argument
   const int q0 = qt * kBM, qw = q0 + wave * 32, qi = qw + n;
 
@@ -174,10 +175,10 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dq_kernel(const Params p) {
   const i32x4 rv = rsrc_words(p.v + krow0 * ROWB, (uint32_t)Skv * ROWB);
 
   const int rows_end = min(q0 + kBM, Sq);
-  const int kv_end = CAUSAL ? min(Skv, rows_end) : Skv;
+  const int kv_end = CAUSAL ? min(Skv, max(0, rows_end - kv_start)) : Skv;
   const int ntot = (kv_end + kBN - 1) / kBN;
   const bool wave_live = qw < Sq;
-  const int w_kv_end = CAUSAL ? min(Skv, min(qw + 32, Sq)) : Skv;
+  const int w_kv_end = CAUSAL ? min(Skv, max(0, min(qw + 32, Sq) - kv_start)) : Skv;
   const int w_ntiles = wave_live ? (w_kv_end + kBN - 1) / kBN : 0;
 
   // Q and dO rows as B operands (rows >= Sq read as zero); D_i = dO_i . O_i.
@@ -258,7 +259,7 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dq_kernel(const Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = u * kBN + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-          const bool ok = key < Skv && (!CAUSAL || key <= qi);
+          const bool ok = key < Skv && (!CAUSAL || key + kv_start <= qi);
           s[i] = ok ? s[i] : -INFINITY;
         }
       }
@@ -280,7 +281,7 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dq_kernel(const Params p) {
       }
     }
   };
-  const int first_masked = CAUSAL ? min(Skv / kBN, (qw + 1) / kBN) : Skv / kBN;
+  const int first_masked = CAUSAL ? min(Skv / kBN, max(0, qw - kv_start + 1) / kBN) : Skv / kBN;
   int u = 0;
   for (; u < min(first_masked, ntot); ++u) {
     sync(u);
@@ -348,7 +349,7 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dkdv_kernel(const Params p)
   const int b = bhg / nhg, h0 = (bhg % nhg) * p.hpw, hk = h0 / p.group;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, n = lane & 31;
-  const int Sq = p.Sq, Skv = p.Skv, Hq = p.Hq;
+  const int Sq = p.Sq, Skv = p.Skv, Hq = p.Hq, kv_start = p.kv_start;
   const float c = p.c, scale = p.scale;   // locals: lambdas must not capture the kernel argument
   const char* const gq = p.q;
   const char* const gdo = p.dout;
@@ -388,13 +389,13 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dkdv_kernel(const Params p)
 
   // Query tiles: for each of the workgroup's query heads, tiles [qt_begin, nqt).
   const int nqt = (Sq + kBN - 1) / kBN;
-  const int qt_begin = CAUSAL ? min(nqt, k0 / kBN) : 0;
+  const int qt_begin = CAUSAL ? min(nqt, (k0 + kv_start) / kBN) : 0;
   const int per_head = nqt - qt_begin;
   const int ntot = per_head * p.hpw;
   // This wave: tiles before w_qt_begin hold no row >= its first key; from
   // w_qt_full on every row is >= its last key.
-  const int w_qt_begin = CAUSAL ? kw / kBN : 0;
-  const int w_qt_full = CAUSAL ? (kw + 31 + kBN - 1) / kBN : 0;
+  const int w_qt_begin = CAUSAL ? (kw + kv_start) / kBN : 0;
+  const int w_qt_full = CAUSAL ? (kw + kv_start + 31 + kBN - 1) / kBN : 0;
 
   constexpr int PW = 2 * T::NINSTR / kWaves;
   static_assert(PW >= 1 && PW * kWaves == 2 * T::NINSTR, "tile copies must split evenly over waves");
@@ -458,7 +459,7 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dkdv_kernel(const Params p)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qrow = qt * kBN + 32 * qb + 8 * (i >> 2) + 4 * g + (i & 3);
-          s[i] = kj <= qrow ? s[i] : -INFINITY;
+          s[i] = kj + kv_start <= qrow ? s[i] : -INFINITY;
         }
       }
       // P = exp2(c s - LSE log2 e) and dS = P (dP - D), in place, with the
@@ -600,14 +601,14 @@ extern "C" int64_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, 
   return bwd_workspace(B, Hq, Hkv, Sq, Skv, D);
 }
 
-extern "C" attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                                  const float* lse, void* dq, void* dk, void* dv,
-                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
-                                  float scale, int causal, attn_dtype_t dtype,
-                                  void* workspace, int64_t workspace_bytes, void* stream) {
+static attn_status_t bwd_launch(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                                float scale, int causal, attn_dtype_t dtype, int64_t kv_start,
+                                void* workspace, int64_t workspace_bytes, void* stream) {
   if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
-  if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0) return ATTN_ERR_SHAPE;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || kv_start < 0) return ATTN_ERR_SHAPE;
   if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return ATTN_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
   const bool any_q = B > 0 && Hq > 0 && Sq > 0;
@@ -623,6 +624,7 @@ extern "C" attn_status_t attn_bwd(const void* q, const void* k, const void* v, c
   const int64_t rowb = 2 * D;
   if ((Sq + kBM) * rowb >= lim || (Skv + kBM) * rowb >= lim || (Skv + kBM) * D * 4 >= lim || (Sq + kBM) * 8 >= lim)
     return ATTN_ERR_OVERFLOW;
+  if (kv_start + Skv + kBM >= ((int64_t)1 << 30)) return ATTN_ERR_OVERFLOW;   // key positions stay below 2^30
   const int64_t need = bwd_workspace(B, Hq, Hkv, Sq, Skv, D);
   if (need > 0 && (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
   const int64_t n_qtiles = (Sq + kBM - 1) / kBM, n_kblocks = (Skv + kBM - 1) / kBM;
@@ -653,6 +655,7 @@ extern "C" attn_status_t attn_bwd(const void* q, const void* k, const void* v, c
   p.hpw = (int)hpw;
   p.n_qtiles = (int)n_qtiles;
   p.n_kblocks = (int)n_kblocks;
+  p.kv_start = (int)kv_start;
   p.c = scale * kLog2e;
   p.scale = scale;
   const hipStream_t st = (hipStream_t)stream;
@@ -682,4 +685,22 @@ extern "C" attn_status_t attn_bwd(const void* q, const void* k, const void* v, c
     }
   }
   return ATTN_OK;
+}
+
+extern "C" attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                  const float* lse, void* dq, void* dk, void* dv,
+                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                                  float scale, int causal, attn_dtype_t dtype,
+                                  void* workspace, int64_t workspace_bytes, void* stream) {
+  return bwd_launch(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, 0,
+                    workspace, workspace_bytes, stream);
+}
+
+extern "C" attn_status_t attn_bwd_chunk(const void* q, const void* k, const void* v, const void* out,
+                                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                                        float scale, int causal, attn_dtype_t dtype, int64_t kv_start,
+                                        void* workspace, int64_t workspace_bytes, void* stream) {
+  return bwd_launch(q, k, v, out, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, kv_start,
+                    workspace, workspace_bytes, stream);
 }

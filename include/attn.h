@@ -214,7 +214,25 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        float scale, int causal, attn_dtype_t dtype,
                        void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Bytes of workspace attn_bwd needs: 8 per query row (its LSE and D), plus
+/*
+ * attn_bwd_chunk — attn_bwd for one key chunk of a longer key sequence, the
+ * backward of attn_fwd_chunk: key j of k / v sits at position j + kv_start
+ * (>= 0) and, with causal, is allowed for query i iff j + kv_start <= i. out
+ * and lse must be those of the attention over ALL keys (the merged result of
+ * the chunks, as after the out/LSE merge on the page "feat(attention): add
+ * strict bitwise ROCm path", Summary table), so that P and D are the full
+ * softmax's. Then dk and dv are this chunk's gradients and dq is the chunk's
+ * contribution: the full dQ is the sum of dq over the chunks. kv_start = 0 is
+ * attn_bwd. Errors as attn_bwd; ATTN_ERR_SHAPE for kv_start < 0,
+ * ATTN_ERR_OVERFLOW when kv_start + Skv reaches 2^30.
+ */
+attn_status_t attn_bwd_chunk(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                             float scale, int causal, attn_dtype_t dtype, int64_t kv_start,
+                             void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_bwd and attn_bwd_chunk need: 8 per query row (its LSE and D), plus
  * fp32 partial dK and dV per query head (8 * B * Hq * Skv * D) when grouped KV
  * heads are split over workgroups; -1 on invalid arguments. */
 int64_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D);

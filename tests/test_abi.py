@@ -144,6 +144,20 @@ def test_backward_fail_closed_validation(L, args, status):
     assert st == status, (args, ha.STATUS.get(st, st))
 
 
+@pytest.mark.parametrize("args,status", [
+    (dict(kv_start=-1), 2),
+    (dict(kv_start=(1 << 30) - 100), 6),
+    (dict(kv_start=5, D=96), 3),
+    (dict(kv_start=5, dq=None), 1),
+])
+def test_backward_chunk_fail_closed_validation(L, args, status):
+    a = dict(q=P, dq=P, D=128, kv_start=0)
+    a.update(args)
+    st = ha.attn_bwd_chunk(a["q"], P, P, P, P, P, a["dq"], P, P, 1, 4, 2, 100, 100, a["D"], 0.1, 1, 0,
+                           a["kv_start"], P, 1 << 40, 0)
+    assert st == status, (args, ha.STATUS.get(st, st))
+
+
 def test_backward_workspace_size():
     # 8 bytes of row statistics per query row, padded to 256 bytes ...
     assert ha.attn_bwd_workspace_bytes(1, 2, 2, 100, 100, 128) == 1792

@@ -106,6 +106,34 @@ def test_backward_matches_oracle(case):
         assert (f64(dK)[:, :, Sq:] == 0).all() and (f64(dV)[:, :, Sq:] == 0).all()
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Sq,Skv,bounds", [(700, 700, (0, 300, 700)), (700, 700, (0, 64, 333, 700)),
+                                           (500, 900, (0, 256, 257, 900))])
+def test_backward_key_chunks_sum_to_full(causal, Sq, Skv, bounds):
+    """attn_bwd_chunk over key chunks, each with the full softmax's O and LSE: the
+    chunks' dQ add up to the full dQ and their dK / dV are the full ones' slices
+    (the backward of a context-parallel split of the keys)."""
+    say(f"case backward chunks causal={causal} Sq={Sq} Skv={Skv} bounds={bounds}")
+    B, Hq, Hkv, D = 1, 4, 2, 128
+    q, k, v, do = bf16_inputs(B, Hq, Hkv, Sq, Skv, D, seed=55 + len(bounds))
+    scale = 1 / math.sqrt(D)
+    Q, K, V, dO = (to_dev(x, "bf16") for x in (q, k, v, do))
+    O, L = ha.forward(Q, K, V, scale=scale, causal=causal)
+    dq = np.zeros((B, Hq, Sq, D))
+    dks, dvs = [], []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        Kc, Vc = K[:, :, a:b].contiguous(), V[:, :, a:b].contiguous()
+        gq, gk, gv = ha.backward(Q, Kc, Vc, O, dO, L, scale=scale, causal=causal, kv_start=a)
+        torch.cuda.synchronize()
+        dq += f64(gq)
+        dks.append(f64(gk))
+        dvs.append(f64(gv))
+    rq, rk, rv = oracle.attention_backward(dec(q), dec(k), dec(v), dec(do), scale, causal)
+    check_grad(dq, rq, "dQ (sum over chunks)")
+    check_grad(np.concatenate(dks, axis=2), rk, "dK (chunks)")
+    check_grad(np.concatenate(dvs, axis=2), rv, "dV (chunks)")
+
+
 def test_backward_is_deterministic_and_batch_invariant():
     say("case backward determinism / batch composition")
     B, Hq, Hkv, S, D = 3, 4, 2, 333, 128
