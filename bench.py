@@ -276,7 +276,7 @@ def main():
                          "headline); causal workloads run causal")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no sharding or collectives); use --gpus 1",
+        print("bench.py: the attention path runs on one GPU only (no sharding or collectives); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
