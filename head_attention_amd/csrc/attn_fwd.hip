@@ -420,21 +420,63 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
     }
   } else {
     // Per tile and wave: skip it (no key of it is allowed for any of the
-    // wave's rows), take it whole, or mask it.
+    // wave's rows), take it whole, or mask it. The whole tiles of a wave form
+    // at most two runs of the tile sequence (inside the sink keys; inside
+    // every row's window), which get a loop of their own without mask code;
+    // the tiles around them take the per-tile decision.
     const int r_lo = qw, r_hi = min(qw + 31, p.Sq - 1);
     const int cap = CAUSAL ? r_hi : 0x7fffffff;
-    for (int u = 0; u < ntot; ++u) {
+    auto general = [&](int u) __attribute__((always_inline)) {
       sync(u);
-      if (!wave_live) continue;
+      if (!wave_live) return;
       const int t = tile_of(u);
       const int k_lo = t * kBN + kv_start, k_hi = k_lo + kBN - 1;
       const bool any = t * kBN < Skv && ((k_hi >= r_lo - wl && k_lo <= min(r_hi + wr, cap)) || (k_lo < sink && k_lo <= cap));
-      if (!any) continue;
+      if (!any) return;
       const bool whole = t * kBN + kBN <= Skv && (!CAUSAL || k_hi <= r_lo) &&
                          ((k_lo >= r_hi - wl && k_hi <= r_lo + wr) || k_hi < sink);
       if (whole) step(u, std::false_type{});
       else step(u, std::true_type{});
+    };
+    // First position in the sequence whose tile index is >= x.
+    auto seq_lb = [&](int x) __attribute__((always_inline)) {
+      if (x <= tA0) return 0;
+      if (x < tA0 + nA) return x - tA0;
+      if (nB == 0 || x <= tB0) return nA;
+      if (x < tB0 + nB) return nA + x - tB0;
+      return ntot;
+    };
+    auto fdiv = [](int a) { return a >= 0 ? a / kBN : -((-a + kBN - 1) / kBN); };   // floor(a / kBN)
+    const int t_full = Skv / kBN - 1;                            // last tile with no key past Skv
+    const int hi_lim = CAUSAL ? r_lo : min(r_lo + wr, 0x3fffffff);
+    const int ts_hi = min(t_full, fdiv(min(sink - 1, CAUSAL ? r_lo : 0x3fffffff) - kv_start - (kBN - 1)));
+    const int tw_lo = max(0, -fdiv(-(r_hi - wl - kv_start)));    // ceil
+    const int tw_hi = min(t_full, fdiv(hi_lim - kv_start - (kBN - 1)));
+    int us0 = 0, us1 = 0, uw0 = 0, uw1 = 0;
+    if (wave_live) {
+      if (ts_hi >= 0) us1 = seq_lb(ts_hi + 1);
+      if (tw_hi >= tw_lo) {
+        uw0 = seq_lb(tw_lo);
+        uw1 = seq_lb(tw_hi + 1);
+      }
+      if (uw1 <= uw0) uw0 = uw1 = us1;                           // no window run
+      if (uw0 <= us1) {                                           // the runs touch: one run
+        us1 = max(us1, uw1);
+        uw0 = uw1 = us1;
+      }
     }
+    int u = 0;
+    for (; u < us0; ++u) general(u);
+    for (; u < us1; ++u) {
+      sync(u);
+      step(u, std::false_type{});
+    }
+    for (; u < uw0; ++u) general(u);
+    for (; u < uw1; ++u) {
+      sync(u);
+      step(u, std::false_type{});
+    }
+    for (; u < ntot; ++u) general(u);
   }
 
 
