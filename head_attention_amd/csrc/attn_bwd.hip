@@ -455,13 +455,8 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dkdv_kernel(const Params p)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(qs + off), kf[dc], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(dos + off), lds_b128(vsm + (vb ^ (dc << 5))), dp, 0, 0, 0);
       }
-      if constexpr (decltype(masked_c)::value) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qrow = qt * kBN + 32 * qb + 8 * (i >> 2) + 4 * g + (i & 3);
-          s[i] = kj + kv_start <= qrow ? s[i] : -INFINITY;
-        }
-      }
+      // causal: row 32 qb + 8 j + 4 g + t of the tile sees this lane's key iff 8 j + t >= thr
+      [[maybe_unused]] const int thr = kj + kv_start - (qt * kBN + 32 * qb + 4 * g);
       // P = exp2(c s - LSE log2 e) and dS = P (dP - D), in place, with the
       // statistics of this lane's rows 32 qb + 8 j + 4 g + (0..3)
 #pragma unroll
@@ -473,7 +468,8 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dkdv_kernel(const Params p)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int i = 4 * j + t;
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l2[t]));
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l2[t]));
+          if constexpr (decltype(masked_c)::value) pv = 8 * j + t >= thr ? pv : 0.f;
           s[i] = pv;
           dp[i] = pv * (dp[i] - dl[t]);
         }
