@@ -202,3 +202,36 @@ def test_backward_llm_full_size_properties():
     want = dod.reshape(w.B, w.Hkv, w.Hq // w.Hkv, w.Sq, w.D).sum(axis=(2, 3))
     got = dv.sum(axis=2)
     assert np.abs(got - want).max() <= 1e-2 * np.abs(dv).sum(axis=2).max()
+
+
+def test_backward_graph_capture_replays():
+    """attn_bwd (dQ, dK/dV and group-sum kernels, no memsets) captured in a HIP graph on a
+    side stream: every replay, with eager work in between, gives the eager bits."""
+    say("case backward hip graph capture")
+    B, Hq, Hkv, S, D = 1, 4, 2, 500, 128
+    q, k, v, do = bf16_inputs(B, Hq, Hkv, S, S, D, seed=31)
+    scale = 1 / math.sqrt(D)
+    Q, K, V, dO = (to_dev(x, "bf16") for x in (q, k, v, do))
+    O, L = ha.forward(Q, K, V, scale=scale, causal=True)
+    ref = ha.backward(Q, K, V, O, dO, L, scale=scale, causal=True)
+    need = ha.attn_bwd_workspace_bytes(B, Hq, Hkv, S, S, D)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        st = ha.attn_bwd(Q, K, V, O, dO, L, dQ, dK, dV, B, Hq, Hkv, S, S, D, scale, True, ha.ATTN_BF16,
+                         ws, need, side.cuda_stream)
+    assert st == 0
+    for rep in range(3):
+        dQ.fill_(float("nan"))
+        dK.fill_(float("nan"))
+        dV.fill_(float("nan"))
+        ws.fill_(255)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((dQ, dK, dV), ref):
+            assert torch.equal(got, want), f"replay {rep} differs from the eager result"
+
