@@ -70,6 +70,20 @@ def algorithmic_bytes(B, Hq, Hkv, Sq, Skv, D, elt):
     return (B * Hq * Sq * D + 2 * B * Hkv * Skv * D) * elt + B * Hq * Sq * D * 2 + B * Hq * Sq * 4
 
 
+def kernel_source_hash():
+    """sha256 of the forward kernel's code (attn_fwd.hip then device_common.h) with
+    // comments and blank lines removed, so that comment edits keep the hash."""
+    import hashlib
+    import re
+    code = []
+    for f in ("attn_fwd.hip", "device_common.h"):
+        for ln in open(os.path.join(ROOT, "head_attention_amd", "csrc", f)).read().split("\n"):
+            ln = re.sub(r"//.*$", "", ln).rstrip()
+            if ln.strip():
+                code.append(ln)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE counter summary.
 
@@ -78,11 +92,10 @@ def measured_traffic():
     """
     import hashlib
     prof = os.path.join(ROOT, "profiles", "attn_fwd_kernel_video_dit_B1H5S75600D128_hbm_traffic.md")
-    srcs = [os.path.join(ROOT, "head_attention_amd", "csrc", f) for f in ("attn_fwd.hip", "device_common.h")]
     try:
         line = [l for l in open(prof) if l.startswith("traffic_json: ")][0]
         rec = json.loads(line[len("traffic_json: "):])
-        if rec["source_sha256"] != hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest():
+        if rec["source_sha256"] != kernel_source_hash():
             return {}
         return rec["bytes_per_launch"]
     except (OSError, IndexError, KeyError, ValueError):

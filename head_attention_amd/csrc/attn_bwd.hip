@@ -30,6 +30,9 @@
 //  * Tiles that are read both as rows and through the transposing
 //    ds_read_b64_tr_b16 use an XOR swizzle that is bank-conflict free for both
 //    access patterns.
+//  * Key chunks: key j sits at position j + kv_start (causal: allowed for
+//    query i iff j + kv_start <= i). Given the full softmax's O and LSE, the
+//    call for one chunk yields that chunk's dK, dV and its share of dQ.
 //  * Grouped KV heads: a dK/dV workgroup either loops over every query head of
 //    its KV head (sums in registers), or, when that leaves too few workgroups
 //    for the chip, takes one query head and writes fp32 partials that a small

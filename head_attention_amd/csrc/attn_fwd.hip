@@ -38,6 +38,16 @@
 //  * Causal: a workgroup only loads the key tiles its rows can see; within
 //    them a wave skips tiles entirely above its rows and masks only tiles that
 //    cross its diagonal. Causal grids run the longest query tiles first.
+//  * Local attention (window sides and sink keys; the window_size_left /
+//    window_size_right arguments of the page "F8 fmha ASM gfx950", Test
+//    Result section): a workgroup loads only the sink tiles and the tiles its
+//    rows' windows cover (one or two runs of the tile sequence); each wave
+//    takes the tiles that are wholly inside its rows' windows or sinks in
+//    loops without mask code and decides skip / whole / masked only for the
+//    tiles around them.
+//  * Key splits (split-KV): workgroups of one query tile may take disjoint
+//    whole-tile key ranges, each written as a normalised fp32 partial with
+//    its LSE; merge_splits_kernel combines them by LSE on the device.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
