@@ -271,6 +271,94 @@ def bench_backward(args, w):
         "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "workspace_bytes": need}), flush=True)
 
 
+SWEEP_FWD = [  # B, H, S, D, causal, dtype
+    (16, 8, 1024, 128, False, "bf16"), (4, 8, 4096, 128, False, "bf16"), (1, 8, 16384, 128, False, "bf16"),
+    (1, 4, 65536, 128, False, "bf16"), (16, 8, 1024, 128, True, "bf16"), (4, 8, 4096, 128, True, "bf16"),
+    (1, 8, 16384, 128, True, "bf16"), (1, 4, 65536, 128, True, "bf16"),
+    (4, 8, 4096, 64, False, "bf16"), (1, 8, 16384, 64, False, "bf16"), (1, 8, 16384, 64, True, "bf16"),
+    (4, 8, 4096, 128, False, "fp8"), (1, 8, 16384, 128, False, "fp8"), (1, 4, 65536, 128, False, "fp8"),
+    (1, 8, 16384, 128, True, "fp8"), (1, 8, 16384, 64, False, "fp8"),
+]
+SWEEP_BWD = [  # B, Hq, Hkv, S, D, causal
+    (4, 8, 8, 2048, 128, True), (1, 32, 8, 4096, 128, True), (1, 8, 8, 16384, 128, True),
+    (1, 8, 8, 8192, 128, False), (1, 8, 8, 16384, 64, True), (1, 32, 8, 4096, 64, True),
+]
+
+
+def sweep(args):
+    """Forward and backward throughput over a grid of shapes (random N(0,1) inputs drawn
+    on the GPU; timing only). Prints one markdown table line per shape."""
+    import numpy as np
+    import torch
+    import head_attention_amd as ha
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    stream = torch.cuda.current_stream()
+
+    def timed(call, n):
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    print("| pass | B | Hq/Hkv | S | D | mask | dtype | ms | TFLOP/s | of dense peak |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for B, H, S, D, causal, dt in SWEEP_FWD:
+        q = torch.randn(B, H, S, D, device=dev, generator=g)
+        k = torch.randn(B, H, S, D, device=dev, generator=g)
+        v = torch.randn(B, H, S, D, device=dev, generator=g)
+        ds = [None] * 3
+        if dt == "bf16":
+            Q, K, V = (t.to(torch.bfloat16) for t in (q, k, v))
+            code = ha.ATTN_BF16
+        else:
+            sc = [t.abs().max() / 448 for t in (q, k, v)]
+            Q, K, V = ((t / c).to(torch.float8_e4m3fn) for t, c in zip((q, k, v), sc))
+            ds = [c.reshape(1).float() for c in sc]
+            code = ha.ATTN_FP8_E4M3FN
+        del q, k, v
+        O = torch.empty(B, H, S, D, dtype=torch.bfloat16, device=dev)
+        L = torch.empty(B, H, S, dtype=torch.float32, device=dev)
+
+        def call():
+            st = ha.attn_fwd(Q, K, V, O, L, B, H, H, S, S, D, 1 / math.sqrt(D), int(causal), code,
+                             ds[0], ds[1], ds[2], stream.cuda_stream)
+            if st != 0:
+                raise ha.AttnError(st, "attn_fwd")
+        t = timed(call, max(3, min(args.steps, 20)))
+        tf = attn_flops(B, H, S, S, D, causal) / t / 1e12
+        print(f"| fwd | {B} | {H}/{H} | {S} | {D} | {'causal' if causal else 'none'} | {dt} | {t * 1e3:.3f} | "
+              f"{tf:.0f} | {tf / PEAK_TFLOPS['bf16' if dt == 'bf16' else 'fp8']:.3f} |", flush=True)
+        del Q, K, V, O, L
+    for B, Hq, Hkv, S, D, causal in SWEEP_BWD:
+        Q = torch.randn(B, Hq, S, D, device=dev, generator=g).to(torch.bfloat16)
+        K = torch.randn(B, Hkv, S, D, device=dev, generator=g).to(torch.bfloat16)
+        V = torch.randn(B, Hkv, S, D, device=dev, generator=g).to(torch.bfloat16)
+        dO = torch.randn(B, Hq, S, D, device=dev, generator=g).to(torch.bfloat16)
+        O, L = ha.forward(Q, K, V, causal=causal)
+        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+        need = ha.attn_bwd_workspace_bytes(B, Hq, Hkv, S, S, D)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+        def call():
+            st = ha.attn_bwd(Q, K, V, O, dO, L, dQ, dK, dV, B, Hq, Hkv, S, S, D, 1 / math.sqrt(D), int(causal),
+                             ha.ATTN_BF16, ws, need, stream.cuda_stream)
+            if st != 0:
+                raise ha.AttnError(st, "attn_bwd")
+        t = timed(call, max(3, min(args.steps, 20)))
+        tf = 2.5 * attn_flops(B, Hq, S, S, D, causal) / t / 1e12
+        print(f"| bwd | {B} | {Hq}/{Hkv} | {S} | {D} | {'causal' if causal else 'none'} | bf16 | {t * 1e3:.3f} | "
+              f"{tf:.0f} | {tf / PEAK_TFLOPS['bf16']:.3f} |", flush=True)
+        del Q, K, V, dO, O, L, dQ, dK, dV, ws
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +372,8 @@ def main():
     ap.add_argument("--splits", type=int, default=None,
                     help="with --workload: run attn_fwd_splitkv with this many key splits (0 = the "
                          "library's choice) instead of attn_fwd")
+    ap.add_argument("--sweep", action="store_true",
+                    help="print forward and backward throughput over a grid of shapes (markdown table)")
     ap.add_argument("--workload", default=None,
                     help="time one other workload of synth.WORKLOADS instead (a context line, not the "
                          "headline); causal workloads run causal")
@@ -307,6 +397,8 @@ def main():
     import head_attention_amd as ha
     from synth import WORKLOADS, make_inputs
 
+    if args.sweep:
+        return sweep(args)
     if args.workload:
         if args.workload.startswith("bwd"):
             return bench_backward(args, WORKLOADS[args.workload])
