@@ -130,9 +130,14 @@ def cpu_baseline(inp, w, budget_s):
             break
     t = time.perf_counter() - t0
     fl = 4.0 * done * w.Skv * w.D
+    cpu = "unknown CPU"
+    try:
+        cpu = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
+    except (OSError, IndexError):
+        pass
     return {"value": round(fl / t / 1e12, 6), "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} query rows x all {w.Skv} keys of the {inp['fmt']} B1 H5 S75600 D128 workload "
-                      f"(fp64 numpy oracle, {t:.1f} s; rows are independent, so the rate scales)"}
+                      f"(fp64 numpy oracle, {t:.1f} s on {cpu}; rows are independent, so the rate scales)"}
 
 
 def bench_workload(args, w, make_inputs):
@@ -490,12 +495,12 @@ def main():
         "per_dtype": {
             "bf16": {"tflops": round(tf_b, 2), "frac_of_peak": round(tf_b / PEAK_TFLOPS["bf16"], 4),
                      "ms_mean": round(tb.mean() * 1e3, 4), "ms_p50": round(float(np.median(tb)) * 1e3, 4),
-                     "ms_p95": round(float(np.percentile(tb, 95)) * 1e3, 4),
+                     "ms_p95": round(float(np.percentile(tb, 95)) * 1e3, 4), "ms_min": round(float(tb.min()) * 1e3, 4),
                      "pages_gbps_convention": round(pages_gbps(B, H, H, S, S, D, 2, tb.mean()), 3),
                      "vs_pages": round(tf_b / PAGES_TFLOPS["bf16"], 4)},
             "fp8": {"tflops": round(tf_8, 2), "frac_of_peak": round(tf_8 / PEAK_TFLOPS["fp8"], 4),
                     "ms_mean": round(t8.mean() * 1e3, 4), "ms_p50": round(float(np.median(t8)) * 1e3, 4),
-                    "ms_p95": round(float(np.percentile(t8, 95)) * 1e3, 4),
+                    "ms_p95": round(float(np.percentile(t8, 95)) * 1e3, 4), "ms_min": round(float(t8.min()) * 1e3, 4),
                     "pages_gbps_convention": round(pages_gbps(B, H, H, S, S, D, 1, t8.mean()), 3),
                     "vs_pages": round(tf_8 / PAGES_TFLOPS["fp8"], 4),
                     "roofline": roof(tf_8, "fp8", t8.mean(), 1)},
