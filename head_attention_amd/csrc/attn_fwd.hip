@@ -12,6 +12,8 @@
 // Design (gfx950 first; nothing here is translated from another kernel):
 //  * One workgroup = 8 wavefronts = 256 query rows of one (batch, head); each
 //    wave owns 32 rows. The grid covers B * Hq * ceil(Sq / 256) workgroups.
+//    A grid that small enough to leave half the CUs idle uses workgroups of 4
+//    wavefronts (128 rows) instead, twice as many of them.
 //  * K and V stream through LDS in tiles of 64 keys, in a ring of kStages
 //    slots filled kStages-1 tiles ahead by buffer_load ... lds (global -> LDS
 //    without VGPRs); one workgroup barrier per tile publishes a tile and
@@ -114,8 +116,11 @@ struct Tile {
   }
 };
 
-template <int D, bool CAUSAL, bool FP8, bool WIN>
-__global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
+template <int D, bool CAUSAL, bool FP8, bool WIN, int NW>
+__global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
+  constexpr int kW = NW;            // waves per workgroup (8, or 4 for grids that leave CUs idle)
+  constexpr int kThr = 64 * NW;
+  constexpr int kRows = 32 * NW;    // query rows per workgroup
   using T = Tile<D, FP8>;
   constexpr int ROWB = T::ROWB;
   constexpr int NDB = D / 32;                       // 32-wide output column blocks
@@ -142,7 +147,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   const int b = bh / p.Hq, h = bh % p.Hq, hk = h / p.group;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, n = lane & 31;
-  const int q0 = qt * kBM, qw = q0 + wave * 32, qi = qw + n;
+  const int q0 = qt * kRows, qw = q0 + wave * 32, qi = qw + n;
 
   const size_t qrow0 = (size_t)(b * p.Hq + h) * (size_t)p.Sq;
   const size_t krow0 = (size_t)(b * p.Hkv + hk) * (size_t)p.Skv + (size_t)(Skv > 0 ? s0 : 0);
@@ -159,7 +164,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   }
 
   // Key tiles this workgroup needs, and those this wave needs.
-  const int rows_end = min(q0 + kBM, p.Sq);
+  const int rows_end = min(q0 + kRows, p.Sq);
   const int kv_end = CAUSAL ? min(Skv, max(0, rows_end - kv_start)) : Skv;
   const int ntiles = (kv_end + kBN - 1) / kBN;
   const bool wave_live = qw < p.Sq;
@@ -210,7 +215,7 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   // Clear the ring once, so that tail rows never expose uninitialised LDS.
-  for (int i = threadIdx.x; i < kStages * 2 * T::BYTES / 16; i += kThreads)
+  for (int i = threadIdx.x; i < kStages * 2 * T::BYTES / 16; i += kThr)
     *(LDS_AS u32x4*)(smem + i * 16) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
@@ -218,8 +223,8 @@ __global__ void __launch_bounds__(kThreads) attn_fwd_kernel(const Params p) {
   // (K first, then V) are split evenly, piece w*PW .. w*PW+PW-1 to wave w. LDS
   // is written lane-linearly, so the swizzle is applied to the global address
   // each lane fetches.
-  constexpr int PW = 2 * T::NINSTR / kWaves;   // pieces per wave per tile
-  static_assert(PW >= 1 && PW * kWaves == 2 * T::NINSTR, "tile pieces must split evenly over waves");
+  constexpr int PW = 2 * T::NINSTR / kW;   // pieces per wave per tile
+  static_assert(PW >= 1 && PW * kW == 2 * T::NINSTR, "tile pieces must split evenly over waves");
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int u) __attribute__((always_inline)) {
     const int key0 = tile_of(u) * kBN;
@@ -577,10 +582,15 @@ __global__ void __launch_bounds__(256) merge_splits_kernel(const float* __restri
 
 typedef void (*kernel_fn)(Params);
 
+template <int D, bool FP8, int NW>
+kernel_fn pick_nw(bool causal, bool win) {
+  if (win) return causal ? attn_fwd_kernel<D, true, FP8, true, NW> : attn_fwd_kernel<D, false, FP8, true, NW>;
+  return causal ? attn_fwd_kernel<D, true, FP8, false, NW> : attn_fwd_kernel<D, false, FP8, false, NW>;
+}
+
 template <int D, bool FP8>
-kernel_fn pick(bool causal, bool win) {
-  if (win) return causal ? attn_fwd_kernel<D, true, FP8, true> : attn_fwd_kernel<D, false, FP8, true>;
-  return causal ? attn_fwd_kernel<D, true, FP8, false> : attn_fwd_kernel<D, false, FP8, false>;
+kernel_fn pick(bool causal, bool win, int nw) {
+  return nw == 4 ? pick_nw<D, FP8, 4>(causal, win) : pick_nw<D, FP8, 8>(causal, win);
 }
 
 }  // namespace hat
@@ -588,6 +598,17 @@ kernel_fn pick(bool causal, bool win) {
 using namespace hat;
 
 static constexpr int64_t kMaxSplits = 256;
+
+// Compute units of the current device (queried once per device).
+static int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 64) cache[dev] = cus;
+  return cus;
+}
 
 static int64_t splitkv_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t D, int64_t nsplit) {
   return nsplit <= 1 ? 0 : nsplit * B * Hq * Sq * (D + 1) * 4;
@@ -620,12 +641,16 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   // Key positions stay below 2^30, so position arithmetic (with the unbounded
   // window sides held as 2^30) never leaves int range.
   if (kv_start + Skv + kBN >= ((int64_t)1 << 30)) return ATTN_ERR_OVERFLOW;
-  const int64_t n_qtiles = (Sq + kBM - 1) / kBM;
   if (nsplit < 1 || nsplit > kMaxSplits) return ATTN_ERR_SHAPE;
   // Key splits are whole tiles; fewer tiles than splits leaves fewer splits.
   const int64_t ktiles = any_kv ? (Skv + kBN - 1) / kBN : 0;
   const int64_t per = ktiles > 0 ? (ktiles + nsplit - 1) / nsplit : 1;
   const int64_t nsp = ktiles > 0 ? (ktiles + per - 1) / per : 1;
+  // Workgroups of 8 waves (256 query rows); 4 waves (128 rows) when an unsplit
+  // grid of 256-row tiles fills at most half the CUs, so that the doubled grid
+  // of half-size workgroups still runs in one round.
+  const int nw = nsp == 1 && 2 * B * Hq * ((Sq + kBM - 1) / kBM) <= (int64_t)device_cus() ? 4 : 8;
+  const int64_t n_qtiles = (Sq + 32 * nw - 1) / (32 * nw);
   const int64_t rows = B * Hq * Sq;
   if (nsp > 1) {
     if (!workspace) return ATTN_ERR_WORKSPACE;
@@ -665,9 +690,9 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   p.sink = (int)std::min(sink, kUnbounded);
 
   kernel_fn fn;
-  if (dtype == ATTN_BF16) fn = D == 128 ? pick<128, false>(causal, win) : pick<64, false>(causal, win);
-  else fn = D == 128 ? pick<128, true>(causal, win) : pick<64, true>(causal, win);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, p);
+  if (dtype == ATTN_BF16) fn = D == 128 ? pick<128, false>(causal, win, nw) : pick<64, false>(causal, win, nw);
+  else fn = D == 128 ? pick<128, true>(causal, win, nw) : pick<64, true>(causal, win, nw);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * nw), 0, (hipStream_t)stream, p);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   if (nsp > 1) {
     const unsigned mgrid = (unsigned)((rows + 15) / 16);
@@ -688,9 +713,7 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
 // of at least 16 key tiles, that bring the rounds to 90 % occupancy (merge
 // traffic and per-workgroup start-up grow with the split count).
 static int64_t auto_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int cus = device_cus();
   const int64_t nwg = B * Hq * ((Sq + kBM - 1) / kBM);
   const int64_t ktiles = (Skv + kBN - 1) / kBN;
   auto occupancy = [&](int64_t sp) {
