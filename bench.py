@@ -472,7 +472,7 @@ def main():
     def roof(tf, dt, t, elt):
         return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
                 "frac": round(tf / PEAK_TFLOPS[dt], 4), "traffic": traffic.get(dt),
-                "kernel": f"attn_fwd_kernel<128,false,{'true' if dt == 'fp8' else 'false'},false>",
+                "kernel": f"attn_fwd_kernel<128,false,{'true' if dt == 'fp8' else 'false'},false,8>",
                 "mean_launch_ms": round(t * 1e3, 4),
                 "algorithmic_bytes": algorithmic_bytes(B, H, H, S, S, D, elt)}
 
