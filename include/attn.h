@@ -1,5 +1,7 @@
 /*
- * attn.h — C ABI of the MI355X (gfx950) fused attention forward.
+ * attn.h — C ABI of the MI355X (gfx950) fused attention forward with LSE, its
+ * key-chunk, local-attention and split-KV forms, the deterministic backward,
+ * and the host-side LSE merge.
  *
  * The operation is the fused scaled-dot-product attention forward that also
  * returns the per-row log-sum-exp, as used through the flash/efficient SDPA
