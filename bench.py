@@ -164,8 +164,11 @@ def bench_workload(args, w, make_inputs):
     dt = ha.ATTN_BF16 if fmt == "bf16" else ha.ATTN_FP8_E4M3FN
     nsplit = None
     if args.splits is not None:
-        nsplit = args.splits or ha.attn_splitkv_auto_splits(w.B, w.Hq, w.Sq, w.Skv, w.D)
-        wbytes = ha.attn_splitkv_workspace_bytes(w.B, w.Hq, w.Sq, w.D, nsplit)
+        # 0 goes to the library as is (its choice may split only a last, partly filled
+        # round of query tiles); the workspace is sized for the count that choice uses
+        nsplit = args.splits
+        sized = nsplit or ha.attn_splitkv_auto_splits(w.B, w.Hq, w.Sq, w.Skv, w.D)
+        wbytes = ha.attn_splitkv_workspace_bytes(w.B, w.Hq, w.Sq, w.D, sized)
         ws = torch.empty(max(wbytes, 16), dtype=torch.uint8, device=dev)
 
     local = w.window_left >= 0 or w.window_right >= 0 or w.sink > 0
@@ -211,11 +214,11 @@ def bench_workload(args, w, make_inputs):
         "config": {"workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Skv{w.Skv} D{w.D} "
                                f"{'causal' if causal else 'non-causal'}"
                                + (f", window {w.window_left}/{w.window_right}, sink {w.sink}" if local else "")
-                               + (f", {nsplit} key splits" if nsplit else ""), "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                               + (f", {nsplit} key splits" if nsplit else ", library-chosen key splits" if nsplit == 0 else ""), "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "causal": causal,
                    **({"window_left": w.window_left, "window_right": w.window_right, "sink": w.sink} if local else {})},
         "ms_mean": round(float(tl.mean()) * 1e3, 4), "ms_p50": round(float(np.median(tl)) * 1e3, 4),
-        "frac_of_peak": round(tf / PEAK_TFLOPS[dtn], 4), "key_splits": nsplit or 1,
+        "frac_of_peak": round(tf / PEAK_TFLOPS[dtn], 4), "key_splits": nsplit if nsplit is not None else 1,
         "workgroups": w.B * w.Hq * ((w.Sq + 255) // 256)}), flush=True)
 
 

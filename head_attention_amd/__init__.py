@@ -210,15 +210,17 @@ def forward_splitkv(q, k, v, n_splits=0, scale=None, causal=False, q_descale=Non
     for t in (q, k, v):
         if t.dtype != q.dtype or not t.is_contiguous() or t.device.type != "cuda":
             raise ValueError("q, k, v must be contiguous GPU tensors of one dtype")
-    if n_splits == 0:
-        n_splits = attn_splitkv_auto_splits(B, Hq, Sq, Skv, D)
+    # n_splits = 0 is passed on as the library's choice (which may split only the
+    # query tiles of a last, partly filled round); the workspace is sized for the
+    # split count that choice uses.
+    sized = attn_splitkv_auto_splits(B, Hq, Sq, Skv, D) if n_splits == 0 else n_splits
     if out is None:
         out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    need = attn_splitkv_workspace_bytes(B, Hq, Sq, D, n_splits)
+    need = attn_splitkv_workspace_bytes(B, Hq, Sq, D, sized)
     if need < 0:
         raise AttnError(2, "attn_splitkv_workspace_bytes")
     if workspace is None and need > 0:

@@ -81,10 +81,15 @@ struct Params {
   const float* vd;
   // Key splits: workgroup blockIdx.x / (B * Hq * n_qtiles) takes keys
   // [split * split_len, + split_len). With o32 set, each split writes its
-  // normalised fp32 O and its LSE to o32 / lse32 at split * B*Hq*Sq rows.
+  // normalised fp32 O and its LSE to o32 / lse32, rows [split * part_rows, +
+  // part_rows) holding global rows [part_row0, part_row0 + part_rows).
+  // Tail mode (n_full >= 0, non-causal): workgroups [0, n_full) take whole
+  // query tiles 0 .. n_full-1 and write out / lse directly; the later ones
+  // take the nsplit key splits of each remaining (tail) tile.
   int nsplit, split_len;
   float* o32;
   float* lse32;
+  int n_full, part_rows, part_row0;
   // Local attention (instances with WIN): key position j (absolute, i.e.
   // local key + kv_start) is allowed for query i iff i - wl <= j <= i + wr, or
   // j < sink; causal additionally requires j <= i. Unbounded sides hold 2^30.
@@ -130,8 +135,21 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
 
   const int BH = p.B * p.Hq;
-  const int per_split = BH * p.n_qtiles;
-  const int split = (int)(blockIdx.x / per_split), bid = (int)(blockIdx.x % per_split);
+  int split, bid;
+  if (p.n_full >= 0) {
+    if ((int)blockIdx.x < p.n_full) {
+      split = -1;   // whole tile, direct output
+      bid = (int)blockIdx.x;
+    } else {
+      const int r = (int)blockIdx.x - p.n_full;
+      split = r % p.nsplit;
+      bid = p.n_full + r / p.nsplit;
+    }
+  } else {
+    const int per_split = BH * p.n_qtiles;
+    split = (int)(blockIdx.x / per_split);
+    bid = (int)(blockIdx.x % per_split);
+  }
   int bh, qt;
   if (CAUSAL) {  // longest rows first
     qt = p.n_qtiles - 1 - bid / BH;
@@ -141,8 +159,8 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     qt = bid % p.n_qtiles;
   }
   // This workgroup's keys: [s0, s0 + Skv) of the head; causal positions shift by s0.
-  const int s0 = split * p.split_len;
-  const int Skv = max(0, min(p.Skv - s0, p.split_len));
+  const int s0 = split < 0 ? 0 : split * p.split_len;
+  const int Skv = split < 0 ? p.Skv : max(0, min(p.Skv - s0, p.split_len));
   const int kv_start = p.kv_start + s0;
   const int b = bh / p.Hq, h = bh % p.Hq, hk = h / p.group;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -497,10 +515,11 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
 
   // ---- epilogue: O = O_acc * oscale / l (bf16), LSE = ln2 * (m + log2 l) ----
   if (!wave_live) return;
+  const int qi_full = qi;
   const float ltot = xor32_sum(l);
   const float inv = ltot > 0.f ? oscale / ltot : 0.f;
   const float lse = ltot > 0.f ? (m + __log2f(ltot) - kPre) * 0.69314718055994531f : -INFINITY;
-  if (p.o32 == nullptr) {
+  if (p.o32 == nullptr || split < 0) {
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + qrow0 * (size_t)(D * 2), (uint32_t)p.Sq * D * 2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -516,9 +535,11 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
     }
   } else {
-    // one key split: normalised fp32 O and the split's LSE, for the merge kernel
-    const size_t prow0 = (size_t)split * (size_t)BH * (size_t)p.Sq + qrow0;
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o32 + prow0 * D, (uint32_t)p.Sq * D * 4);
+    // one key split: normalised fp32 O and the split's LSE, for the merge kernel;
+    // rows of this tile from its first row q0 (rows >= Sq fall outside the range)
+    const size_t prow0 = (size_t)split * (size_t)p.part_rows + (qrow0 + (size_t)q0 - (size_t)p.part_row0);
+    const int qi = qi_full - q0;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o32 + prow0 * D, (uint32_t)(p.Sq - q0) * D * 4);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -529,7 +550,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
         __builtin_amdgcn_raw_buffer_store_b128(w, ro, (qi * D + col) * 4, 0, 0);
       }
     if (g == 0) {
-      const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse32 + prow0, (uint32_t)p.Sq * 4);
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse32 + prow0, (uint32_t)(p.Sq - q0) * 4);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
     }
   }
@@ -619,7 +640,8 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
                             float scale, int causal, attn_dtype_t dtype,
                             const float* qd, const float* kd, const float* vd, int64_t kv_start,
                             int64_t nsplit, void* workspace, int64_t workspace_bytes, void* stream,
-                            int64_t window_left = -1, int64_t window_right = -1, int64_t sink = 0) {
+                            int64_t window_left = -1, int64_t window_right = -1, int64_t sink = 0,
+                            bool tail_only = false) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3FN) return ATTN_ERR_DTYPE;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || kv_start < 0) return ATTN_ERR_SHAPE;
@@ -646,19 +668,32 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   const int64_t ktiles = any_kv ? (Skv + kBN - 1) / kBN : 0;
   const int64_t per = ktiles > 0 ? (ktiles + nsplit - 1) / nsplit : 1;
   const int64_t nsp = ktiles > 0 ? (ktiles + per - 1) / per : 1;
+  const bool win = window_left >= 0 || window_right >= 0 || sink > 0;
+  // Tail mode: only the query tiles of the grid's last, partly filled round of
+  // workgroups are split (non-causal, no window).
+  const bool tail = tail_only && nsp > 1 && !causal && !win;
   // Workgroups of 8 waves (256 query rows); 4 waves (128 rows) when an unsplit
   // grid of 256-row tiles fills at most half the CUs, so that the doubled grid
   // of half-size workgroups still runs in one round.
   const int nw = nsp == 1 && 2 * B * Hq * ((Sq + kBM - 1) / kBM) <= (int64_t)device_cus() ? 4 : 8;
   const int64_t n_qtiles = (Sq + 32 * nw - 1) / (32 * nw);
   const int64_t rows = B * Hq * Sq;
+  const int64_t ntiles = B * Hq * n_qtiles;
+  int64_t n_full = -1, part_rows = rows, part_row0 = 0, grid = ntiles * nsp;
+  if (tail) {
+    const int64_t cus = device_cus();
+    n_full = ntiles / cus * cus;
+    if (n_full == 0 || n_full == ntiles) return ATTN_ERR_SHAPE;
+    part_row0 = (n_full / n_qtiles) * Sq + (n_full % n_qtiles) * (32 * nw);
+    part_rows = rows - part_row0;
+    grid = n_full + (ntiles - n_full) * nsp;
+  }
   if (nsp > 1) {
     if (!workspace) return ATTN_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 15) return ATTN_ERR_WORKSPACE;
-    if (workspace_bytes < splitkv_bytes(B, Hq, Sq, D, nsp)) return ATTN_ERR_WORKSPACE;
+    if (workspace_bytes < nsp * part_rows * (D + 1) * 4) return ATTN_ERR_WORKSPACE;
     if ((Sq + kBM) * D * 4 >= lim) return ATTN_ERR_OVERFLOW;
   }
-  const int64_t grid = B * Hq * n_qtiles * nsp;
   if (B * Hq >= lim || grid >= lim || (rows + 16) / 16 >= lim) return ATTN_ERR_OVERFLOW;
 
   Params p;
@@ -682,9 +717,11 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   p.nsplit = (int)nsp;
   p.split_len = nsp > 1 ? (int)(per * kBN) : (int)Skv;
   p.o32 = nsp > 1 ? (float*)workspace : nullptr;
-  p.lse32 = nsp > 1 ? (float*)workspace + nsp * rows * D : nullptr;
+  p.lse32 = nsp > 1 ? (float*)workspace + nsp * part_rows * D : nullptr;
+  p.n_full = (int)n_full;
+  p.part_rows = (int)part_rows;
+  p.part_row0 = (int)part_row0;
   constexpr int64_t kUnbounded = (int64_t)1 << 30;
-  const bool win = window_left >= 0 || window_right >= 0 || sink > 0;
   p.wl = (int)(window_left < 0 ? kUnbounded : std::min(window_left, kUnbounded));
   p.wr = (int)(window_right < 0 ? kUnbounded : std::min(window_right, kUnbounded));
   p.sink = (int)std::min(sink, kUnbounded);
@@ -695,13 +732,15 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * nw), 0, (hipStream_t)stream, p);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   if (nsp > 1) {
-    const unsigned mgrid = (unsigned)((rows + 15) / 16);
+    const unsigned mgrid = (unsigned)((part_rows + 15) / 16);
+    char* out_part = (char*)out + part_row0 * D * 2;
+    float* lse_part = lse + part_row0;
     if (D == 128)
       hipLaunchKernelGGL(merge_splits_kernel<128>, dim3(mgrid), dim3(256), 0, (hipStream_t)stream,
-                         p.o32, p.lse32, (char*)out, lse, (long long)rows, (int)nsp);
+                         p.o32, p.lse32, out_part, lse_part, (long long)part_rows, (int)nsp);
     else
       hipLaunchKernelGGL(merge_splits_kernel<64>, dim3(mgrid), dim3(256), 0, (hipStream_t)stream,
-                         p.o32, p.lse32, (char*)out, lse, (long long)rows, (int)nsp);
+                         p.o32, p.lse32, out_part, lse_part, (long long)part_rows, (int)nsp);
     if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   }
   return ATTN_OK;
@@ -712,7 +751,7 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
 // chip is power-bound, so idle CUs cost little); else the fewest splits, each
 // of at least 16 key tiles, that bring the rounds to 90 % occupancy (merge
 // traffic and per-workgroup start-up grow with the split count).
-static int64_t auto_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv) {
+static int64_t auto_full_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv) {
   const int cus = device_cus();
   const int64_t nwg = B * Hq * ((Sq + kBM - 1) / kBM);
   const int64_t ktiles = (Skv + kBN - 1) / kBN;
@@ -724,6 +763,39 @@ static int64_t auto_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv) {
   for (int64_t sp = 2; sp <= 16 && ktiles / sp >= 16; ++sp)
     if (occupancy(sp) >= 0.9) return sp;
   return 1;
+}
+
+// Tail splits: when whole rounds of 256-row query tiles fill every CU and a
+// last round is left partly empty, split only that round's tiles into k key
+// ranges, k in 2..8 (each at least 16 key tiles), so that the k-times more,
+// k-times shorter workgroups finish sooner than one more whole round: the k
+// minimising ceil(tail * k / CUs) / k, if that is at most 0.85 of a round.
+// Returns 0 when no such k exists.
+static int64_t tail_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv) {
+  const int64_t cus = device_cus();
+  const int64_t ntiles = B * Hq * ((Sq + kBM - 1) / kBM);
+  const int64_t ntail = ntiles % cus;
+  if (ntiles < cus || ntail == 0) return 0;
+  const int64_t ktiles = (Skv + kBN - 1) / kBN;
+  int64_t best = 0;
+  double best_t = 0.85 + 1e-9;
+  for (int64_t k = 2; k <= 8 && ktiles / k >= 16; ++k) {
+    const double t = (double)((ntail * k + cus - 1) / cus) / (double)k;
+    if (t < best_t - 1e-9) {
+      best = k;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
+// The split count attn_fwd_splitkv uses for n_splits = 0: the whole-grid split
+// when one helps, else a tail split (non-causal calls only), else 1.
+static int64_t auto_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv) {
+  const int64_t f = auto_full_splits(B, Hq, Sq, Skv);
+  if (f > 1) return f;
+  const int64_t t = tail_splits(B, Hq, Sq, Skv);
+  return t >= 2 ? t : 1;
 }
 
 extern "C" attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -770,7 +842,20 @@ extern "C" attn_status_t attn_fwd_splitkv(const void* q, const void* k, const vo
                                           const float* q_descale, const float* k_descale, const float* v_descale,
                                           int64_t n_splits, void* workspace, int64_t workspace_bytes, void* stream) {
   if (n_splits < 0) return ATTN_ERR_SHAPE;
-  if (n_splits == 0) n_splits = (B > 0 && Hq > 0 && Sq > 0 && Skv > 0) ? auto_splits(B, Hq, Sq, Skv) : 1;
+  bool tail_only = false;
+  if (n_splits == 0) {
+    n_splits = 1;
+    if (B > 0 && Hq > 0 && Sq > 0 && Skv > 0) {
+      n_splits = auto_full_splits(B, Hq, Sq, Skv);
+      if (n_splits <= 1 && !causal) {
+        const int64_t t = tail_splits(B, Hq, Sq, Skv);
+        if (t >= 2) {
+          n_splits = t;
+          tail_only = true;
+        }
+      }
+    }
+  }
   return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, q_descale, k_descale,
-                v_descale, 0, n_splits, workspace, workspace_bytes, stream);
+                v_descale, 0, n_splits, workspace, workspace_bytes, stream, -1, -1, 0, tail_only);
 }

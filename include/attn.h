@@ -155,10 +155,15 @@ attn_status_t attn_merge_lse2_host(const uint16_t* o1, const float* lse1,
  *
  *   n_splits        >= 1 splits of whole 64-key tiles (fewer are used when Skv
  *                   has fewer tiles); 1 is attn_fwd itself (no workspace is
- *                   read). 0 lets the library choose
- *                   (attn_splitkv_auto_splits). At most 256.
+ *                   read). 0 lets the library choose: a split of every query
+ *                   tile when the grid leaves compute units idle, else, for
+ *                   non-causal calls whose whole rounds of query tiles fill
+ *                   every compute unit, a split of only the query tiles of the
+ *                   last, partly filled round (the other rows are written
+ *                   exactly as attn_fwd writes them), else none. At most 256.
  *   workspace       device buffer of at least attn_splitkv_workspace_bytes(B,
- *                   Hq, Sq, D, n_splits) bytes, 16-byte aligned, owned by the
+ *                   Hq, Sq, D, n) bytes, n = n_splits, or for n_splits = 0
+ *                   n = attn_splitkv_auto_splits(...), 16-byte aligned, owned by the
  *                   caller; its contents on entry do not matter and are
  *                   overwritten. It may be NULL when one split is used.
  *   workspace_bytes its size in bytes.
@@ -177,10 +182,15 @@ attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void
 int64_t attn_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t D, int64_t n_splits);
 
 /* The split count attn_fwd_splitkv uses for n_splits = 0 on the current
- * device: 1 when the B * Hq * ceil(Sq / 256) query tiles already fill at
- * least 85 % of their last round over the compute units, else the fewest
- * splits (each at least 16 key tiles, at most 16) that reach 90 %, or 1 if
- * none does. -1 on invalid arguments. Queries the current HIP device. */
+ * device, for sizing its workspace. With T = B * Hq * ceil(Sq / 256) query
+ * tiles of 256 rows (split calls always use 256-row tiles): when T leaves more
+ * than 15 % of its last round over the compute units idle, the fewest splits
+ * of every tile (each at least 16 key tiles, at most 16) that reach 90 %;
+ * else, when T is at least one round and the last round is partly empty, the
+ * k in 2..8 (each at least 16 key tiles) that splits only that round's tiles
+ * into the least time, ceil(tail * k / CUs) / k rounds, if that is at most
+ * 0.85 of a round (used by non-causal calls only; a causal call then runs
+ * unsplit); else 1. -1 on invalid arguments. Queries the current HIP device. */
 int64_t attn_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int64_t D);
 
 /*

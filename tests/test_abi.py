@@ -180,9 +180,18 @@ def test_splitkv_workspace_size():
 
 
 def test_splitkv_auto_split_choice():
-    # 1480 video-DiT workgroups fill 256 CUs, 228 (window-30 shape) nearly do: no split.
-    assert ha.attn_splitkv_auto_splits(1, 5, 75600, 75600, 128) == 1
+    # 1480 video-DiT query tiles fill 5 rounds of 256 CUs and 200 tiles of a sixth: only those
+    # 200 are split, 5 ways (1000 short workgroups need 0.8 of a round; 2-4 ways would need 1).
+    assert ha.attn_splitkv_auto_splits(1, 5, 75600, 75600, 128) == 5
+    # 228 tiles (window-30 shape) nearly fill one round: no split.
     assert ha.attn_splitkv_auto_splits(1, 12, 4680, 51480, 128) == 1
+    # 258 tiles fill only half of their second round: the whole grid is split (9 x 258 =
+    # 2322 workgroups, 91 % of 10 rounds).
+    assert ha.attn_splitkv_auto_splits(1, 2, 33000, 33000, 128) == 9
+    # 460 tiles: one full round and 204 tiles; those are split 5 ways (0.8 of a round).
+    assert ha.attn_splitkv_auto_splits(1, 4, 29440, 29440, 128) == 5
+    # 280 tiles, 33 key tiles: 2 ways (each split keeps at least 16 key tiles).
+    assert ha.attn_splitkv_auto_splits(1, 40, 1700, 2100, 128) == 2
     # 185 (an eighth of the video-DiT queries) fill 72 %: four splits make 740 = 96 % of 3 rounds.
     assert ha.attn_splitkv_auto_splits(1, 5, 9450, 75600, 128) == 4
     assert ha.attn_splitkv_auto_splits(2, 8, 2048, 2048, 128) == 2

@@ -92,3 +92,45 @@ def test_splitkv_video_dit_shard_full_size_auto():
     Oref, Lref = oracle_ref(inp, w.scale, False, rows=rows)
     check_bf16(O[:, :, rows], L[:, :, rows], Oref, Lref, what="video_dit_shard split")
     assert float(np.abs(O - Ou).max()) <= 8e-3
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3fn"])
+def test_splitkv_tail_only_split(fmt):
+    """With the library's choice at 280 query tiles on 256 CUs, only the last 24 tiles
+    (one partial round) are split over their keys; the rest are computed whole. Every
+    row against the oracle, and against attn_fwd."""
+    B, Hq, Hkv, Sq, Skv, D = 1, 40, 40, 1700, 2100, 128
+    assert ha.attn_splitkv_auto_splits(B, Hq, Sq, Skv, D) == 2
+    say(f"case splitkv tail-only split {fmt}")
+    inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, fmt, seed=77)
+    scale = 1 / math.sqrt(D)
+    O, L, Ou, Lu = run_split(inp, scale, False, 0)
+    Oref, Lref = oracle_ref(inp, scale, False)
+    if fmt == "bf16":
+        check_bf16(O, L, Oref, Lref, what="tail split")
+    else:
+        check_fp8(O, L, Oref, Lref, what="tail split")
+    # rows of whole tiles are the unsplit kernel's bits; tail rows agree to fp32 rounding
+    whole_rows = (256 // 7) * Sq + (256 % 7) * 256          # first row of the first tail tile
+    flatO, flatOu = O.reshape(-1, D), Ou.reshape(-1, D)
+    assert np.array_equal(flatO[:whole_rows], flatOu[:whole_rows])
+    assert float(np.abs(flatO[whole_rows:] - flatOu[whole_rows:]).max()) <= (8e-3 if fmt == "bf16" else 4e-2)
+
+
+def test_splitkv_tail_only_split_long_rows():
+    """460 tiles (one full round of 256, then 204 tail tiles split 5 ways over 460 key
+    tiles): whole-tile rows equal the unsplit kernel's bits; sampled rows on both sides
+    of the first tail tile and in the last head against the oracle."""
+    B, Hq, Hkv, Sq, Skv, D = 1, 4, 4, 29440, 29440, 128
+    assert ha.attn_splitkv_auto_splits(B, Hq, Sq, Skv, D) == 5
+    say("case splitkv tail-only split, long rows")
+    inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, "bf16", seed=78)
+    scale = 1 / math.sqrt(D)
+    O, L, Ou, Lu = run_split(inp, scale, False, 0)
+    first_tail = 256 - 2 * 115                               # tile 256 is head 2, query tile 26
+    rows = np.array([0, 100, first_tail * 256 - 1, first_tail * 256, first_tail * 256 + 200, Sq - 1])
+    Oref, Lref = oracle_ref(inp, scale, False, rows=rows)
+    check_bf16(O[:, :, rows], L[:, :, rows], Oref, Lref, what="tail split long rows")
+    assert np.array_equal(O[:, :2], Ou[:, :2])               # heads 0 and 1: whole tiles only
+    assert np.array_equal(O[:, 2, :first_tail * 256], Ou[:, 2, :first_tail * 256])
+    assert float(np.abs(O - Ou).max()) <= 8e-3
