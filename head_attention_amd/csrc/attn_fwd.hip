@@ -290,6 +290,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     __syncthreads();
     if (u + kStages - 1 < ntot) issue(u + kStages - 1);
   };
+  [[maybe_unused]] int pkeep[kBN / 64][8] = {};   // fp8: last P words, reused as conversion targets
   // The tile's scores, softmax and P V for this wave. Masked tiles take the
   // element mask; the others are compiled without it, so no mask work is ever
   // speculated on them.
@@ -417,9 +418,13 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
           const int j = 4 * w, kb = 2 * kq + (j >> 4), i = j & 15;
-          int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i], s[kb][i + 1], 0, false);
+          // the first conversion writes the low half-word only; the previous
+          // tile's word is passed as the high half (overwritten next) so that no
+          // register has to be cleared for it
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i], s[kb][i + 1], pkeep[kq][w], false);
           x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i + 2], s[kb][i + 3], x, true);
           pw[w] = x;
+          pkeep[kq][w] = x;
         }
         const i32x8 pf = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
 #pragma unroll
