@@ -266,7 +266,11 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   f32x16 o[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  // l, the lane's share of the row sum, gathers one fp32 partial per tile in
+  // fp64: once m has reached a dominant key, the remaining tiles each add about
+  // one fp32 ulp of l, and over 10^5 tiles those roundings would bias l.
+  float m = -INFINITY;
+  double l = 0.0;
 
   // Per-lane constant parts of the LDS operand addresses.
   // K operand (A of S^T): row 32*kb + n, logical chunk per dc.
@@ -366,7 +370,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sraw[kb][i]);
       const float mnew = fmaxf(m, xor32_max(mx) * c);
       const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 when m was -inf
-      l *= alpha;
+      l *= (double)alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
       m = mnew;
@@ -381,7 +385,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
           rs += pv;
         }
     }
-    l += rs;
+    l += (double)rs;
 
     // ---- O^T += V^T P^T ----
     if constexpr (!FP8) {
@@ -521,7 +525,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   // ---- epilogue: O = O_acc * oscale / l (bf16), LSE = ln2 * (m + log2 l) ----
   if (!wave_live) return;
   const int qi_full = qi;
-  const float ltot = xor32_sum(l);
+  const float ltot = xor32_sum((float)l);
   const float inv = ltot > 0.f ? oscale / ltot : 0.f;
   const float lse = ltot > 0.f ? (m + __log2f(ltot) - kPre) * 0.69314718055994531f : -INFINITY;
   if (p.o32 == nullptr || split < 0) {
@@ -755,18 +759,32 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
 // tiles already occupy at least 85 % of the last round of workgroups (the
 // chip is power-bound, so idle CUs cost little); else the fewest splits, each
 // of at least 16 key tiles, that bring the rounds to 90 % occupancy (merge
-// traffic and per-workgroup start-up grow with the split count).
+// traffic and per-workgroup start-up grow with the split count). A grid of
+// less than one round that 16 splits cannot bring to 90 % (a few query tiles
+// against many keys) takes the count up to kMaxSplits with the least
+// estimated time, rounds * (key tiles per split + 2 tiles of workgroup
+// start-up) + 3 tiles for the merge launch, or the fewest within 3 % of it.
+// (A grid of one round or more is left to tail_splits.)
 static int64_t auto_full_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv) {
-  const int cus = device_cus();
+  const int64_t cus = device_cus();
   const int64_t nwg = B * Hq * ((Sq + kBM - 1) / kBM);
   const int64_t ktiles = (Skv + kBN - 1) / kBN;
   auto occupancy = [&](int64_t sp) {
     const int64_t w = nwg * sp;
     return (double)w / (double)(cus * ((w + cus - 1) / cus));
   };
-  if (nwg <= 0 || occupancy(1) >= 0.85) return 1;
+  if (nwg <= 0 || ktiles <= 0 || occupancy(1) >= 0.85) return 1;
   for (int64_t sp = 2; sp <= 16 && ktiles / sp >= 16; ++sp)
     if (occupancy(sp) >= 0.9) return sp;
+  if (nwg >= cus) return 1;
+  const int64_t maxsp = std::min<int64_t>(kMaxSplits, ktiles / 16);
+  auto cost = [&](int64_t sp) {
+    return (double)((nwg * sp + cus - 1) / cus) * (double)((ktiles + sp - 1) / sp + 2) + (sp > 1 ? 3.0 : 0.0);
+  };
+  double best = cost(1);
+  for (int64_t sp = 2; sp <= maxsp; ++sp) best = std::min(best, cost(sp));
+  for (int64_t sp = 1; sp <= maxsp; ++sp)
+    if (cost(sp) <= 1.03 * best) return sp;
   return 1;
 }
 

@@ -59,8 +59,11 @@ typedef enum {
   ATTN_ERR_HEAD_DIM = 3,  /* D is not 64 or 128 */
   ATTN_ERR_DTYPE = 4,     /* unknown attn_dtype_t */
   ATTN_ERR_ALIGN = 5,     /* q, k, v or out not 16-byte aligned, or lse not 4-byte aligned */
-  ATTN_ERR_OVERFLOW = 6,  /* one head's slice reaches 2^31 bytes, kv_start + Skv reaches 2^30,
-                             or the grid is too large */
+  ATTN_ERR_OVERFLOW = 6,  /* one head's slice, padded by one tile, reaches 2^31 bytes
+                             ((Sq + 256) * D * 2 for q/out, (Skv + 64) * D * elt for k/v:
+                             D128 allows Sq <= 8388351 and Skv <= 8388543 in bf16,
+                             16777151 in fp8), kv_start + Skv reaches 2^30, or the grid
+                             is too large */
   ATTN_ERR_SCALE = 7,     /* scale is not finite or not > 0 */
   ATTN_ERR_HIP = 8,       /* the kernel launch failed */
   ATTN_ERR_WORKSPACE = 9  /* attn_fwd_splitkv / attn_bwd: workspace NULL, misaligned, or too small */
@@ -183,14 +186,20 @@ int64_t attn_splitkv_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t 
 
 /* The split count attn_fwd_splitkv uses for n_splits = 0 on the current
  * device, for sizing its workspace. With T = B * Hq * ceil(Sq / 256) query
- * tiles of 256 rows (split calls always use 256-row tiles): when T leaves more
- * than 15 % of its last round over the compute units idle, the fewest splits
- * of every tile (each at least 16 key tiles, at most 16) that reach 90 %;
- * else, when T is at least one round and the last round is partly empty, the
- * k in 2..8 (each at least 16 key tiles) that splits only that round's tiles
- * into the least time, ceil(tail * k / CUs) / k rounds, if that is at most
- * 0.85 of a round (used by non-causal calls only; a causal call then runs
- * unsplit); else 1. -1 on invalid arguments. Queries the current HIP device. */
+ * tiles of 256 rows (split calls always use 256-row tiles) and every split
+ * at least 16 key tiles:
+ *   - when T leaves more than 15 % of its last round over the compute units
+ *     idle, the fewest splits of every tile, at most 16, that reach 90 %;
+ *     if none does and T is below one round (a few query tiles against many
+ *     keys), the count up to 256 with the least estimated time,
+ *     rounds * (key tiles per split + 2) + 3 for the merge, or the fewest
+ *     within 3 % of that;
+ *   - else, when T is at least one round and the last round is partly empty,
+ *     the k in 2..8 that splits only that round's tiles into the least time,
+ *     ceil(tail * k / CUs) / k rounds, if that is at most 0.85 of a round
+ *     (used by non-causal calls only; a causal call then runs unsplit);
+ *   - else 1.
+ * -1 on invalid arguments. Queries the current HIP device. */
 int64_t attn_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Sq, int64_t Skv, int64_t D);
 
 /*

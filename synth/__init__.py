@@ -13,4 +13,6 @@ from .inputs import (  # noqa: F401
     to_bf16_bits,
     quant_e4m3fn_per_tensor,
     make_inputs,
+    random_codes,
+    plant_needles,
 )

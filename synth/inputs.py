@@ -123,6 +123,33 @@ def quant_e4m3fn_per_tensor(x: torch.Tensor):
     return codes, descale
 
 
+def random_codes(shape, fmt: str, seed: int) -> np.ndarray:
+    """Stored-format codes drawn directly as bits, for tensors too large for
+    ``normal`` (10^9 elements): a random sign and mantissa and one of the
+    exponents of [2^-7, 2) for bf16 (uint16), of [2^-3, 2) for e4m3fn (uint8);
+    never zero, never a NaN or infinity."""
+    rng = np.random.default_rng(int(seed))
+    if fmt == "bf16":
+        r = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+        return (r & np.uint16(0x807F)) | ((np.uint16(120) + ((r >> np.uint16(7)) & np.uint16(7))) << np.uint16(7))
+    if fmt == "e4m3fn":
+        r = rng.integers(0, 1 << 8, size=shape, dtype=np.uint8)
+        return (r & np.uint8(0x87)) | ((np.uint8(4) + ((r >> np.uint8(3)) & np.uint8(3))) << np.uint8(3))
+    raise ValueError(fmt)
+
+
+def plant_needles(q: np.ndarray, k: np.ndarray, positions, fmt: str, steps=None) -> None:
+    """In place on codes from ``random_codes`` ([S, D] views): key row
+    ``positions[r]`` becomes query row r times 2^steps[r] (default 4: the
+    exponent field raised by steps[r], exact; steps in 1..4), so that query r's
+    largest score is with that key."""
+    shift = 7 if fmt == "bf16" else 3
+    for r, pos in enumerate(positions):
+        st = 2 if steps is None else int(steps[r])
+        assert 1 <= st <= 4
+        k[pos] = q[r] + k.dtype.type(st << shift)
+
+
 def make_inputs(w: Workload, fmt: str = None, sq: int = None, skv: int = None):
     """Draw q, k, v for workload ``w`` (optionally with shorter Sq / Skv).
 

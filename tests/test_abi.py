@@ -69,6 +69,10 @@ P = 1 << 20
     (dict(lse=P + 2), 5),
     (dict(Sq=1 << 30), 6),
     (dict(Skv=1 << 30), 6),
+    (dict(Sq=8388352), 6),                   # one past the largest D128 query slice
+    (dict(Skv=8388544), 6),                  # one past the largest D128 bf16 key slice
+    (dict(Skv=16777152, dtype=1), 6),        # one past the largest D128 fp8 key slice
+    (dict(Sq=16776960, D=64), 6),            # one past the largest D64 query slice
     (dict(kv_start=(1 << 30) - 100), 6),     # key positions must stay below 2^30
     (dict(kv_start=(1 << 30) - 65, Skv=1), 6),    # kv_start + Skv + one key tile = 2^30
 ])
@@ -196,6 +200,12 @@ def test_splitkv_auto_split_choice():
     assert ha.attn_splitkv_auto_splits(1, 5, 9450, 75600, 128) == 4
     assert ha.attn_splitkv_auto_splits(2, 8, 2048, 2048, 128) == 2
     assert ha.attn_splitkv_auto_splits(1, 1, 256, 512, 128) == 1      # too few key tiles to split
+    # Grids that 16 splits cannot bring to 90 %: the count with the least estimated time.
+    # One 256-row tile against 16384 key tiles: 249 splits of 66 tiles (the fewest within 3 %
+    # of 256 splits of 64), one round.
+    assert ha.attn_splitkv_auto_splits(1, 1, 256, 1 << 20, 128) == 249
+    assert ha.attn_splitkv_auto_splits(1, 8, 1, 8192, 128) == 8       # 128 key tiles: 8 of 16
+    assert ha.attn_splitkv_auto_splits(1, 1, 300, 3000, 128) == 2     # 47 key tiles: 2 of 23
     assert ha.attn_splitkv_auto_splits(1, 1, 256, 96, 100) == -1
 
 
