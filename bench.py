@@ -293,6 +293,12 @@ SWEEP_BWD = [  # B, Hq, Hkv, S, D, causal
 ]
 
 
+SWEEP_SPLIT = [  # B, H, Sq, Skv, D, dtype: few query tiles against long key ranges
+    (1, 32, 1, 131072, 128, "bf16"), (1, 8, 256, 262144, 128, "bf16"), (1, 1, 256, 1048576, 128, "bf16"),
+    (4, 8, 128, 65536, 128, "fp8"), (1, 2, 4096, 524288, 64, "bf16"),
+]
+
+
 def sweep(args):
     """Forward and backward throughput over a grid of shapes (random N(0,1) inputs drawn
     on the GPU; timing only). Prints one markdown table line per shape."""
@@ -365,6 +371,40 @@ def sweep(args):
         print(f"| bwd | {B} | {Hq}/{Hkv} | {S} | {D} | {'causal' if causal else 'none'} | bf16 | {t * 1e3:.3f} | "
               f"{tf:.0f} | {tf / PEAK_TFLOPS['bf16']:.3f} |", flush=True)
         del Q, K, V, dO, O, L, dQ, dK, dV, ws
+    print()
+    print("| B | H | Sq | Skv | D | dtype | attn_fwd ms | TFLOP/s | splitkv(0) ms | splits | TFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for B, H, Sq, Skv, D, dt in SWEEP_SPLIT:
+        q = torch.randn(B, H, Sq, D, device=dev, generator=g)
+        k = torch.randn(B, H, Skv, D, device=dev, generator=g)
+        v = torch.randn(B, H, Skv, D, device=dev, generator=g)
+        ds = [None] * 3
+        if dt == "bf16":
+            Q, K, V = (t.to(torch.bfloat16) for t in (q, k, v))
+            code = ha.ATTN_BF16
+        else:
+            sc = [t.abs().max() / 448 for t in (q, k, v)]
+            Q, K, V = ((t / c).to(torch.float8_e4m3fn) for t, c in zip((q, k, v), sc))
+            ds = [c.reshape(1).float() for c in sc]
+            code = ha.ATTN_FP8_E4M3FN
+        del q, k, v
+        O = torch.empty(B, H, Sq, D, dtype=torch.bfloat16, device=dev)
+        L = torch.empty(B, H, Sq, dtype=torch.float32, device=dev)
+        nsp = ha.attn_splitkv_auto_splits(B, H, Sq, Skv, D)
+        need = ha.attn_splitkv_workspace_bytes(B, H, Sq, D, nsp)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        res = []
+        for n in (1, 0):
+            def call():
+                st = ha.attn_fwd_splitkv(Q, K, V, O, L, B, H, H, Sq, Skv, D, 1 / math.sqrt(D), 0, code,
+                                         ds[0], ds[1], ds[2], n, ws, need, stream.cuda_stream)
+                if st != 0:
+                    raise ha.AttnError(st, "attn_fwd_splitkv")
+            t = timed(call, max(3, min(args.steps, 20)))
+            res.append((t, attn_flops(B, H, Sq, Skv, D, False) / t / 1e12))
+        print(f"| {B} | {H} | {Sq} | {Skv} | {D} | {dt} | {res[0][0] * 1e3:.3f} | {res[0][1]:.0f} | "
+              f"{res[1][0] * 1e3:.3f} | {nsp} | {res[1][1]:.0f} |", flush=True)
+        del Q, K, V, O, L, ws
 
 
 def main():
