@@ -28,17 +28,28 @@ through dO (no gradient flows into the LSE output).
 
 P is recomputed here from Q and K with its own row maximum; nothing is taken
 from a forward pass of the HIP path.
+
+A backward receives the forward's output next to dO (the dense MHA core of
+that page pairs an mha_fwd with an mha_bwd, and the strict path checks dQ / dK
+/ dV computed from its own out and lse); D_i is the one quantity taken from
+it. ``out`` lets the caller state that O, for example the forward's output
+rounded to bf16: D_i = dO_i . out_i is then formed from it instead of from the
+float64 O = P V (with the exact O both agree). In rows where P is nearly one
+key, dP_ij - D_i is a small difference of two larger numbers, and the rounding
+of O decides it.
 """
 
 import numpy as np
 
 
-def attention_backward(q, k, v, dout, scale, causal=False, kv_start=0, row_block=512):
+def attention_backward(q, k, v, dout, scale, causal=False, kv_start=0, row_block=512, out=None):
     """(dQ [B,Hq,Sq,D], dK [B,Hkv,Skv,D], dV [B,Hkv,Skv,D]) in float64.
 
     q: [B, Hq, Sq, D], k and v: [B, Hkv, Skv, D], dout: [B, Hq, Sq, D], real
     values (already dequantised). Causal keeps key j for query i iff
-    j + kv_start <= i, as in the forward.
+    j + kv_start <= i, as in the forward. ``out`` (optional, [B, Hq, Sq, D]):
+    the forward output the backward is given; D_i = dO_i . out_i then comes
+    from it rather than from the float64 O.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -52,6 +63,9 @@ def attention_backward(q, k, v, dout, scale, causal=False, kv_start=0, row_block
         raise ValueError("inconsistent shapes")
     if kv_start < 0:
         raise ValueError("kv_start must be >= 0")
+    out64 = None if out is None else np.asarray(out, dtype=np.float64)
+    if out64 is not None and out64.shape != q.shape:
+        raise ValueError("out must be [B, Hq, Sq, D]")
     group = Hq // Hkv
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -72,7 +86,7 @@ def attention_backward(q, k, v, dout, scale, causal=False, kv_start=0, row_block
                 e = np.exp(s[live] - m[live, None])
                 P[live] = e / e.sum(axis=1, keepdims=True)
                 dO = dout[b, h, rows]
-                O = P @ V
+                O = P @ V if out64 is None else out64[b, h, rows]
                 dP = dO @ V.T
                 Drow = (dO * O).sum(axis=1)
                 dS = P * (dP - Drow[:, None])

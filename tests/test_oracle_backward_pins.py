@@ -119,6 +119,44 @@ def test_rows_without_keys_have_zero_gradient():
     np.testing.assert_allclose(dv, dv2, rtol=1e-13, atol=1e-15)
 
 
+def test_given_exact_out_equals_default():
+    """Passing the forward's own float64 O as ``out`` changes nothing."""
+    q, k, v, do = rand(2, 4, 9, 5), rand(2, 2, 11, 5), rand(2, 2, 11, 5), rand(2, 4, 9, 5)
+    for causal in (False, True):
+        O, _ = attention_forward(q, k, v, 0.6, causal, kv_start=2)
+        got = attention_backward(q, k, v, do, 0.6, causal, kv_start=2, out=O)
+        ref = attention_backward(q, k, v, do, 0.6, causal, kv_start=2)
+        for a, b in zip(got, ref):
+            np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+def _one_key_closed_form(q, k, v, do, scale, out):
+    """One key: P = 1 for every row, so dV = sum of dO, and dS_i = dO_i . (v - out_i)
+    (dP_i = dO_i . v, D_i = dO_i . out_i), dQ_i = scale dS_i k, dK = scale sum_i dS_i q_i."""
+    B, Hkv, Sq, D = q.shape[0], k.shape[1], q.shape[2], q.shape[3]
+    g = q.shape[1] // Hkv
+    vv = v[:, :, 0, :][:, :, None, None, :]                                    # [B, Hkv, 1, 1, D]
+    ds = ((vv - out.reshape(B, Hkv, g, Sq, D)) * do.reshape(B, Hkv, g, Sq, D)).sum(axis=-1)   # [B, Hkv, g, Sq]
+    kk = k[:, :, 0, :]
+    dq = scale * ds[..., None] * kk[:, :, None, None, :]
+    dk = scale * (ds[..., None] * q.reshape(q.shape[0], k.shape[1], g, q.shape[2], -1)).sum(axis=(2, 3))
+    dv = do.reshape(q.shape[0], k.shape[1], g, q.shape[2], -1).sum(axis=(2, 3))
+    return dq.reshape(q.shape), dk[:, :, None, :], dv[:, :, None, :]
+
+
+def test_given_out_one_key_closed_form():
+    """With a given out that is not the exact O (here v plus noise), one key: the closed
+    form above. A slip that ignores ``out`` or takes it for the wrong head fails it."""
+    q, k, v, do = rand(1, 4, 3, 5), rand(1, 2, 1, 5), rand(1, 2, 1, 5), rand(1, 4, 3, 5)
+    out = np.repeat(v, 2, axis=1).repeat(3, axis=2) + 0.1 * rand(1, 4, 3, 5)
+    got = attention_backward(q, k, v, do, 0.7, False, out=out)
+    ref = _one_key_closed_form(q, k, v, do, 0.7, out)
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+    mut = _load_mutant("O = P @ V if out64 is None else out64[b, h, rows]", "O = P @ V").attention_backward
+    assert not np.allclose(mut(q, k, v, do, 0.7, False, out=out)[0], ref[0])
+
+
 def _load_mutant(old, new):
     import types
     src = open(BWD_FILE).read()
