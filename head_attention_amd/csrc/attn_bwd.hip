@@ -8,6 +8,9 @@
 // softmax(s) recomputed from the forward's LSE, and D_i = dO_i . O_i:
 //     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),
 //     dQ = scale * dS K,   dK = scale * dS^T Q.
+// O is the output the caller passes (the forward's bf16 out): where a row's P
+// is nearly one key, dP - D is a small difference of larger numbers and the
+// rounding of that O decides it.
 //
 // Design (gfx950 first):
 //  * Deterministic by construction: no atomics, every sum in a fixed order,

@@ -12,7 +12,7 @@
 // Design (gfx950 first; nothing here is translated from another kernel):
 //  * One workgroup = 8 wavefronts = 256 query rows of one (batch, head); each
 //    wave owns 32 rows. The grid covers B * Hq * ceil(Sq / 256) workgroups.
-//    A grid that small enough to leave half the CUs idle uses workgroups of 4
+//    A grid small enough to leave half the CUs idle uses workgroups of 4
 //    wavefronts (128 rows) instead, twice as many of them.
 //  * K and V stream through LDS in tiles of 64 keys, in a ring of kStages
 //    slots filled kStages-1 tiles ahead by buffer_load ... lds (global -> LDS
@@ -33,6 +33,8 @@
 //    for a row's first tile, m becomes the exact running max, O and l are
 //    rescaled by exp2(m_old - m_new) and p is formed again (a wave-uniform
 //    branch, rarely taken). p <= 2^8 is well inside bf16 and fp32 range.
+//    Each lane adds its fp32 partial row sum of a tile into an fp64 l, so
+//    that rows over millions of keys keep the tail of their sum.
 //  * fp8: p carries a factor 2^kPre (folded into the exp2 offset), so that
 //    e4m3fn P is at most 2^8 and keeps full precision for the typical
 //    p ~ 1e-2; l sums the same scaled, unrounded fp32 values, and the
