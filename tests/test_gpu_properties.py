@@ -11,7 +11,9 @@
   fully overwritten;
 * identical keys give O = mean(V) and LSE = score + ln(Skv); V = 1 gives O = 1;
   permuting K and V rows together leaves O and LSE unchanged (to tolerance);
-* the launch is capturable in a HIP graph and replays give the eager bits.
+* the launch is capturable in a HIP graph and replays give the eager bits;
+  so are split-KV launches (the attention kernel, its workspace and the merge
+  kernel; whole-grid and tail-only splits) and local-attention launches.
 """
 
 import math
@@ -141,3 +143,51 @@ def test_graph_capture_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(bits(Og), bits(O)) and torch.equal(Lg.cpu(), L.cpu())
+
+
+def test_graph_capture_splitkv_and_window_replays():
+    """One graph holding a whole-grid split-KV launch, a tail-only split-KV launch (the
+    library's choice at 280 query tiles) and a local-attention launch, on a side stream:
+    every replay, with the outputs NaN-filled and the workspaces overwritten in between,
+    gives the eager bits."""
+    say("case hip graph capture: split-KV and window")
+    scale = 1 / math.sqrt(128)
+    Qa, Ka, Va, dsa = dev_inputs(1, 2, 2, 300, 4000, 128, "bf16", 41)          # whole-grid split (auto)
+    Qb, Kb, Vb, dsb = dev_inputs(1, 40, 40, 1700, 2100, 128, "e4m3fn", 42)      # tail-only split (auto)
+    Qc, Kc, Vc, dsc = dev_inputs(1, 4, 2, 900, 900, 128, "bf16", 43)            # window + sink, causal
+    na = ha.attn_splitkv_auto_splits(1, 2, 300, 4000, 128)
+    nb = ha.attn_splitkv_auto_splits(1, 40, 1700, 2100, 128)
+    assert na > 1 and nb == 2
+    wa = torch.empty(ha.attn_splitkv_workspace_bytes(1, 2, 300, 128, na), dtype=torch.uint8, device=DEV)
+    wb = torch.empty(ha.attn_splitkv_workspace_bytes(1, 40, 1700, 128, nb), dtype=torch.uint8, device=DEV)
+    outs = [(torch.empty(1, 2, 300, 128, dtype=torch.bfloat16, device=DEV), torch.empty(1, 2, 300, device=DEV)),
+            (torch.empty(1, 40, 1700, 128, dtype=torch.bfloat16, device=DEV), torch.empty(1, 40, 1700, device=DEV)),
+            (torch.empty(1, 4, 900, 128, dtype=torch.bfloat16, device=DEV), torch.empty(1, 4, 900, device=DEV))]
+
+    def launch(stream):
+        sa = ha.attn_fwd_splitkv(Qa, Ka, Va, outs[0][0], outs[0][1], 1, 2, 2, 300, 4000, 128, scale, 0,
+                                 ha.ATTN_BF16, None, None, None, 0, wa, wa.numel(), stream)
+        sb = ha.attn_fwd_splitkv(Qb, Kb, Vb, outs[1][0], outs[1][1], 1, 40, 40, 1700, 2100, 128, scale, 0,
+                                 ha.ATTN_FP8_E4M3FN, dsb[0], dsb[1], dsb[2], 0, wb, wb.numel(), stream)
+        sc = ha.attn_fwd_window(Qc, Kc, Vc, outs[2][0], outs[2][1], 1, 4, 2, 900, 900, 128, scale, 1,
+                                ha.ATTN_BF16, None, None, None, 0, 200, 0, 70, stream)
+        assert (sa, sb, sc) == (0, 0, 0)
+
+    launch(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = [(bits(o), bits(l)) for o, l in outs]
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        launch(side.cuda_stream)
+    for rep in range(3):
+        for o, l in outs:
+            o.fill_(float("nan"))
+            l.fill_(float("nan"))
+        wa.fill_(255)
+        wb.fill_(255)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (o, l), (ro, rl) in zip(outs, ref):
+            assert torch.equal(bits(o), ro) and torch.equal(bits(l), rl), f"replay {rep} differs from eager"
