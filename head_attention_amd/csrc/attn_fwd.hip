@@ -467,7 +467,9 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     // wave's rows), take it whole, or mask it. The whole tiles of a wave form
     // at most two runs of the tile sequence (inside the sink keys; inside
     // every row's window), which get a loop of their own without mask code;
-    // the tiles around them take the per-tile decision.
+    // the tiles around them are skipped or masked (the masked step gives a
+    // whole tile the same bits, and one step variant per loop keeps these
+    // loops' register pressure down).
     const int r_lo = qw, r_hi = min(qw + 31, p.Sq - 1);
     const int cap = CAUSAL ? r_hi : 0x7fffffff;
     auto general = [&](int u) __attribute__((always_inline)) {
@@ -477,10 +479,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       const int k_lo = t * kBN + kv_start, k_hi = k_lo + kBN - 1;
       const bool any = t * kBN < Skv && ((k_hi >= r_lo - wl && k_lo <= min(r_hi + wr, cap)) || (k_lo < sink && k_lo <= cap));
       if (!any) return;
-      const bool whole = t * kBN + kBN <= Skv && (!CAUSAL || k_hi <= r_lo) &&
-                         ((k_lo >= r_hi - wl && k_hi <= r_lo + wr) || k_hi < sink);
-      if (whole) step(u, std::false_type{});
-      else step(u, std::true_type{});
+      step(u, std::true_type{});
     };
     // First position in the sequence whose tile index is >= x.
     auto seq_lb = [&](int x) __attribute__((always_inline)) {
