@@ -1,6 +1,6 @@
 """Benchmark of the gfx950 attention forward at the video-DiT shape.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-mfma-ceiling]
     python bench.py --copy-calibration MIB   # plain device copy of known size, for HBM counters
 
 One step is the whole hot path over one batch: the bf16 forward at
@@ -13,6 +13,11 @@ Throughput uses the pages' attention-forward convention, 4*B*H*Sq*Skv*D flops
 per launch (halved for causal); ``attn_tflops`` and ``pages_gbps`` reproduce
 the printed fmha summary of the page "F8 fmha ASM gfx950" (Test Result
 section) exactly, which tests/test_oracle_pins.py checks.
+
+After the timed steps (outside them) the line also carries ``mfma_ceiling``:
+what an MFMA-only loop with random operands sustains on the device
+(libmfma_probe.so), and each dtype's fraction of it, beside the fraction of
+the published dense peak that ``roofline`` reports.
 """
 
 import argparse
@@ -299,6 +304,59 @@ SWEEP_SPLIT = [  # B, H, Sq, Skv, D, dtype: few query tiles against long key ran
 ]
 
 
+def mfma_ceiling(dev):
+    """What the matrix cores sustain on this device with nothing else running: the
+    MFMA-only loop of libmfma_probe.so (the attention kernels' bf16 32x32x16 and fp8
+    32x32x64 forms, random register operands rotated per MFMA, two waves per SIMD), timed
+    with HIP events over launches of ~15 ms, after the attention timing. Also the dense
+    peak from the device's CU count and peak clock. None when the probe is not built."""
+    import ctypes
+    import numpy as np
+    import torch
+    path = os.path.join(ROOT, "head_attention_amd", "libmfma_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.mfma_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    L.mfma_probe_launch.restype = ctypes.c_int
+    L.mfma_probe_device.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    L.mfma_probe_device.restype = ctypes.c_int
+    cus, clk = ctypes.c_int(0), ctypes.c_int(0)
+    if L.mfma_probe_device(ctypes.byref(cus), ctypes.byref(clk)) != 0 or cus.value <= 0:
+        return None
+    nblocks = 2 * cus.value
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    src_b = torch.randn(16 * 64 * 8, generator=g, device=dev).to(torch.bfloat16)
+    src_8 = (torch.randn(16 * 64 * 32, generator=g, device=dev) * 32).clamp(-448, 448).to(torch.float8_e4m3fn)
+    out = torch.empty(nblocks * 256, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {"kernel": "MFMA-only loop (libmfma_probe.so): random register operands rotated per MFMA, "
+                     "4 independent accumulators, 2 waves per SIMD", "unit": "TFLOP/s"}
+    for name, fp8, src, iters, fl in (("bf16", 0, src_b, 50000, 32768), ("fp8", 1, src_8, 25000, 131072)):
+        def call():
+            if L.mfma_probe_launch(fp8, nblocks, iters, src.data_ptr(), out.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError("mfma_probe_launch failed")
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(8):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        res[name] = round(nblocks * 4 * iters * 8 * fl / float(np.median(ts)) / 1e12, 1)
+    mhz = clk.value / 1e3
+    res["device"] = {"cus": cus.value, "peak_clock_mhz": mhz,
+                     "dense_peak_bf16": round(cus.value * mhz * 1e6 * 4096 / 1e12, 1),
+                     "dense_peak_fp8": round(cus.value * mhz * 1e6 * 8192 / 1e12, 1)}
+    return res
+
+
 def sweep(args):
     """Forward and backward throughput over a grid of shapes (random N(0,1) inputs drawn
     on the GPU; timing only). Prints one markdown table line per shape."""
@@ -413,6 +471,8 @@ def main():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the MFMA-only ceiling measured after the timed steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB each (scales the "
@@ -551,6 +611,15 @@ def main():
         "roofline": roof(tf_b, "bf16", tb.mean(), 2),
         "cpu_baseline": None,
     }
+    if not args.no_mfma_ceiling:
+        ceil = mfma_ceiling(dev)
+        out["mfma_ceiling"] = ceil
+        if ceil:
+            out["per_dtype"]["bf16"]["frac_of_measured_ceiling"] = round(tf_b / ceil["bf16"], 4)
+            out["per_dtype"]["fp8"]["frac_of_measured_ceiling"] = round(tf_8 / ceil["fp8"], 4)
+            print(f"# MFMA-only ceiling: bf16 {ceil['bf16']} TFLOP/s, fp8 {ceil['fp8']} TFLOP/s; device dense peak "
+                  f"{ceil['device']['dense_peak_bf16']} / {ceil['device']['dense_peak_fp8']} TFLOP/s "
+                  f"({ceil['device']['cus']} CUs at {ceil['device']['peak_clock_mhz']} MHz)", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp_b, wb, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -37,6 +37,24 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), f"missing export {n}"
 
 
+def test_mfma_probe_library_loads_and_refuses_bad_arguments():
+    """The benchmark's MFMA-only probe (a measurement aid beside the attention library)
+    exports its two entry points and rejects bad arguments without launching."""
+    import ctypes
+    path = os.path.join(ROOT, "head_attention_amd", "libmfma_probe.so")
+    if not os.path.exists(path):
+        from head_attention_amd.build import build
+        build()
+    P = ctypes.CDLL(path)
+    P.mfma_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    P.mfma_probe_launch.restype = ctypes.c_int
+    assert hasattr(P, "mfma_probe_device")
+    assert P.mfma_probe_launch(0, 0, 10, 1 << 20, 1 << 20, None) == 1      # no workgroups
+    assert P.mfma_probe_launch(0, 4, 0, 1 << 20, 1 << 20, None) == 1       # no iterations
+    assert P.mfma_probe_launch(1, 4, 10, None, 1 << 20, None) == 1         # no operand buffer
+
+
 def test_status_strings(L):
     for code, name in ha.STATUS.items():
         assert ha.attn_status_string(code).startswith(name)
