@@ -206,6 +206,15 @@ def bench_workload(args, w, make_inputs):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     tl = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+    # short launches: also 100 back-to-back launches between one event pair, so
+    # that per-launch event overhead drops out
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(100):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_loop = e0.elapsed_time(e1) * 1e-3 / 100
     if local:   # 4*D flops per kept (query, key) pair
         flops = 4.0 * w.B * w.Hq * w.D * allowed_pairs(w.Sq, w.Skv, causal, w.window_left, w.window_right, w.sink)
     else:
@@ -223,6 +232,8 @@ def bench_workload(args, w, make_inputs):
                    "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "causal": causal,
                    **({"window_left": w.window_left, "window_right": w.window_right, "sink": w.sink} if local else {})},
         "ms_mean": round(float(tl.mean()) * 1e3, 4), "ms_p50": round(float(np.median(tl)) * 1e3, 4),
+        "ms_p95": round(float(np.percentile(tl, 95)) * 1e3, 4), "ms_min": round(float(tl.min()) * 1e3, 4),
+        "ms_loop100": round(t_loop * 1e3, 4), "tflops_loop100": round(flops / t_loop / 1e12, 2),
         "frac_of_peak": round(tf / PEAK_TFLOPS[dtn], 4), "key_splits": nsplit if nsplit is not None else 1,
         "workgroups": w.B * w.Hq * ((w.Sq + 255) // 256)}), flush=True)
 
@@ -271,6 +282,13 @@ def bench_backward(args, w):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     tl = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(100):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_loop = e0.elapsed_time(e1) * 1e-3 / 100
     flops = 2.5 * attn_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, causal)   # five products of 2*D flops per pair
     tf = flops / tl.mean() / 1e12
     print(json.dumps({
@@ -281,6 +299,8 @@ def bench_backward(args, w):
                                f"{'causal' if causal else 'non-causal'}, deterministic",
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Skv": w.Skv, "D": w.D, "causal": causal},
         "ms_mean": round(float(tl.mean()) * 1e3, 4), "ms_p50": round(float(np.median(tl)) * 1e3, 4),
+        "ms_p95": round(float(np.percentile(tl, 95)) * 1e3, 4), "ms_min": round(float(tl.min()) * 1e3, 4),
+        "ms_loop100": round(t_loop * 1e3, 4), "tflops_loop100": round(flops / t_loop / 1e12, 2),
         "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "workspace_bytes": need}), flush=True)
 
 
