@@ -246,6 +246,12 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   constexpr int PW = 2 * T::NINSTR / kW;   // pieces per wave per tile
   static_assert(PW >= 1 && PW * kW == 2 * T::NINSTR, "tile pieces must split evenly over waves");
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // The K and V buffer descriptors, made wave-uniform once here: lane reads
+  // are convergent operations, which the compiler keeps inside the loop.
+  const i32x4 rkw = i32x4{__builtin_amdgcn_readfirstlane(rk[0]), __builtin_amdgcn_readfirstlane(rk[1]),
+                          __builtin_amdgcn_readfirstlane(rk[2]), __builtin_amdgcn_readfirstlane(rk[3])};
+  const i32x4 rvw = i32x4{__builtin_amdgcn_readfirstlane(rv[0]), __builtin_amdgcn_readfirstlane(rv[1]),
+                          __builtin_amdgcn_readfirstlane(rv[2]), __builtin_amdgcn_readfirstlane(rv[3])};
   auto issue = [&](int u) __attribute__((always_inline)) {
     const int key0 = tile_of(u) * kBN;
     const int slot = u % kStages;
@@ -259,9 +265,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       const int lc = pc ^ (isv ? T::vswz(r) : T::kswz(r));
       const int goff = (key0 + r) * ROWB + lc * 16;
       const unsigned dst = __builtin_amdgcn_readfirstlane(smem_addr + (slot * 2 + (isv ? 1 : 0)) * T::BYTES + c0 * 16);
-      const i32x4 rs = isv ? rv : rk;
-      dma16(i32x4{__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
-                  __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])}, goff, dst);
+      dma16(isv ? rvw : rkw, goff, dst);
     }
   };
 
