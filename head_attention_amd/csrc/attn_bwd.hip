@@ -216,6 +216,9 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dq_kernel(const Params p) {
   constexpr int PW = 2 * T::NINSTR / kWaves;
   static_assert(PW >= 1 && PW * kWaves == 2 * T::NINSTR, "tile copies must split evenly over waves");
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // The K and V descriptors, made wave-uniform once here (lane reads are
+  // convergent operations, which the compiler keeps inside the loop).
+  const i32x4 rkw = sgpr_rsrc(rk), rvw = sgpr_rsrc(rv);
   auto issue = [&](int u) __attribute__((always_inline)) {
     const int key0 = u * kBN, slot = u % S;
 #pragma unroll
@@ -227,7 +230,7 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dq_kernel(const Params p) {
       const int r = cidx / T::CH, pc = cidx % T::CH;
       const int goff = (key0 + r) * ROWB + (pc ^ T::dswz(r)) * 16;
       const unsigned dst = __builtin_amdgcn_readfirstlane(smem_addr + (slot * 2 + (isv ? 1 : 0)) * T::BYTES + c0 * 16);
-      dma16(sgpr_rsrc(isv ? rv : rk), goff, dst);
+      dma16(isv ? rvw : rkw, goff, dst);
     }
   };
 
@@ -406,7 +409,10 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dkdv_kernel(const Params p)
   constexpr int PW = 2 * T::NINSTR / kWaves;
   static_assert(PW >= 1 && PW * kWaves == 2 * T::NINSTR, "tile copies must split evenly over waves");
   auto issue = [&](int u) __attribute__((always_inline)) {
-    const int hh = u / per_head, qt = qt_begin + u % per_head;
+    // head and tile of step u, made wave-uniform right after the division (which
+    // runs on the vector ALU), so that the descriptors below stay scalar
+    const int hh = __builtin_amdgcn_readfirstlane(u / per_head);
+    const int qt = qt_begin + __builtin_amdgcn_readfirstlane(u - hh * per_head);
     const size_t qrow0 = (size_t)(b * Hq + h0 + hh) * (size_t)Sq;
     const unsigned base = ring_addr + (u % S) * C::STAGE;
 #pragma unroll
