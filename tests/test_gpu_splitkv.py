@@ -68,6 +68,47 @@ def test_splitkv_matches_oracle_and_unsplit(case):
     assert dO <= (8e-3 if fmt == "bf16" else 4e-2) and dL <= 1e-4
 
 
+AUTO_CASES = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, fmt: what the library's choice (n_splits = 0) does there
+    (1, 1, 1, 200, 40000, 128, False, "bf16"),     # one query tile: the least-time count (37 splits)
+    (1, 2, 1, 100, 30000, 128, False, "e4m3fn"),   # two tiles, GQA, fp8 (28 splits)
+    (1, 2, 2, 256, 20000, 64, True, "bf16"),       # causal, D64: nearly every split above the diagonal
+    (1, 4, 2, 2000, 8000, 128, False, "bf16"),     # 32 tiles: 7 splits of 18 key tiles
+    (1, 64, 64, 1100, 4000, 64, False, "bf16"),    # 320 tiles: 3 whole-grid splits (94 % of 4 rounds)
+    (1, 40, 40, 1700, 2100, 128, True, "bf16"),    # 280 tiles, causal: the tail count sizes the workspace,
+                                                   # the call itself runs unsplit
+]
+
+
+@pytest.mark.parametrize("case", AUTO_CASES,
+                         ids=[f"B{c[0]}H{c[1]}/{c[2]}S{c[3]}x{c[4]}D{c[5]}c{int(c[6])}{c[7]}" for c in AUTO_CASES])
+def test_splitkv_library_choice(case):
+    """n_splits = 0 with exactly the workspace attn_splitkv_auto_splits sizes, against the
+    oracle and the unsplit kernel."""
+    B, Hq, Hkv, Sq, Skv, D, causal, fmt = case
+    n = ha.attn_splitkv_auto_splits(B, Hq, Sq, Skv, D)
+    say(f"case splitkv library choice {case}: {n} splits")
+    need = ha.attn_splitkv_workspace_bytes(B, Hq, Sq, D, n)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, fmt, seed=11 + Sq + Skv)
+    scale = 1 / math.sqrt(D)
+    O, L, Ou, Lu = run_split(inp, scale, causal, 0, workspace=ws)
+    Oref, Lref = oracle_ref(inp, scale, causal)
+    if fmt == "bf16":
+        check_bf16(O, L, Oref, Lref, what=f"library choice {case}")
+    else:
+        check_fp8(O, L, Oref, Lref, what=f"library choice {case}")
+    fin = np.isfinite(Lu)
+    assert np.array_equal(np.isfinite(L), fin)
+    if causal and B * Hq * ((Sq + 255) // 256) >= 256:
+        # a causal call never takes a tail split: it is the unsplit kernel, bit for bit
+        assert np.array_equal(O, Ou) and np.array_equal(L, Lu)
+    else:
+        assert n > 1
+        assert float(np.abs(O - Ou).max()) <= (8e-3 if fmt == "bf16" else 4e-2)
+        assert float(np.abs(L[fin] - Lu[fin]).max()) <= 1e-4
+
+
 def test_splitkv_ignores_workspace_contents():
     """A workspace full of NaN from an earlier use gives the same result."""
     say("case splitkv dirty workspace")
