@@ -51,12 +51,12 @@ def pages_gbps(B, Hq, Hkv, Sq, Skv, D, elt, seconds):
     return n * elt / seconds / 1e9
 
 
-def allowed_pairs(Sq, Skv, causal, window_left=-1, window_right=-1, sink=0):
+def allowed_pairs(Sq, Skv, causal, window_left=-1, window_right=-1, sink=0, rows=None):
     """Number of (query, key) pairs local attention keeps, counted row by row
     (key j is kept for query i iff it is inside [i - left, i + right] or j < sink,
-    and j <= i with causal)."""
+    and j <= i with causal); over the query rows ``rows`` if given, else all Sq."""
     import numpy as np
-    i = np.arange(Sq, dtype=np.int64)
+    i = np.arange(Sq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
     lo = np.maximum(0, i - window_left) if window_left >= 0 else np.zeros_like(i)
     hi = np.minimum(Skv - 1, i + window_right) if window_right >= 0 else np.full_like(i, Skv - 1)
     if causal:
@@ -111,11 +111,7 @@ def cpu_baseline(inp, w, budget_s):
     """Time the fp64 oracle on a bounded sample of query rows of the same workload."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = _blas_threads()
     q = oracle.dequantise(inp["q"], inp["fmt"], inp["q_descale"])
     k = oracle.dequantise(inp["k"], inp["fmt"], inp["k_descale"])
     v = oracle.dequantise(inp["v"], inp["fmt"], inp["v_descale"])
@@ -135,14 +131,75 @@ def cpu_baseline(inp, w, budget_s):
             break
     t = time.perf_counter() - t0
     fl = 4.0 * done * w.Skv * w.D
-    cpu = "unknown CPU"
-    try:
-        cpu = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
-    except (OSError, IndexError):
-        pass
+    cpu = _cpu_model()
     return {"value": round(fl / t / 1e12, 6), "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} query rows x all {w.Skv} keys of the {inp['fmt']} B1 H5 S75600 D128 workload "
                       f"(fp64 numpy oracle, {t:.1f} s on {cpu}; rows are independent, so the rate scales)"}
+
+
+def _cpu_model():
+    try:
+        return [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
+    except (OSError, IndexError):
+        return "unknown CPU"
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_workload(inp, w, causal, budget_s):
+    """The fp64 oracle on a bounded sample of one workload: blocks of 256 query rows spread
+    over the query range and the heads (causal and windowed rows differ in cost), timed
+    until the budget is spent; the rate counts 4*D flops per kept pair of the sampled rows."""
+    import numpy as np
+    import oracle
+    q = oracle.dequantise(inp["q"], inp["fmt"], inp["q_descale"])
+    k = oracle.dequantise(inp["k"], inp["fmt"], inp["k_descale"])
+    v = oracle.dequantise(inp["v"], inp["fmt"], inp["v_descale"])
+    g = w.Hq // w.Hkv
+    nblk = (w.Sq + 255) // 256
+    order = np.random.default_rng(5).permutation(nblk * w.B * w.Hq)
+    pairs, done, t0 = 0, 0, time.perf_counter()
+    for x in order:
+        b, h, r0 = int(x // (w.Hq * nblk)), int((x // nblk) % w.Hq), int(x % nblk) * 256
+        rows = np.arange(r0, min(r0 + 256, w.Sq))
+        oracle.attention_forward(q[b:b + 1, h:h + 1], k[b:b + 1, h // g:h // g + 1], v[b:b + 1, h // g:h // g + 1],
+                                 w.scale, causal, rows=rows, window_left=w.window_left,
+                                 window_right=w.window_right, sink=w.sink)
+        pairs += allowed_pairs(w.Sq, w.Skv, causal, w.window_left, w.window_right, w.sink, rows=rows)
+        done += len(rows)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    t = time.perf_counter() - t0
+    return {"value": round(4.0 * w.D * pairs / t / 1e12, 6), "unit": "TFLOPS", "cores": int(_blas_threads()),
+            "kind": "oracle",
+            "sample": f"{done} query rows (256-row blocks spread over the rows and heads, {pairs} kept pairs) of "
+                      f"{w.name} (fp64 numpy oracle, {t:.1f} s on {_cpu_model()})"}
+
+
+def cpu_baseline_backward(q, k, v, do, w, causal, budget_s):
+    """The fp64 backward oracle timed over whole query heads (each with its KV head) of the
+    workload until the budget is spent; the rate counts five products, 10*D flops per kept pair."""
+    import oracle
+    g = w.Hq // w.Hkv
+    heads, t0 = 0, time.perf_counter()
+    for h in range(w.B * w.Hq):
+        b, hq = h // w.Hq, h % w.Hq
+        oracle.attention_backward(q[b:b + 1, hq:hq + 1], k[b:b + 1, hq // g:hq // g + 1],
+                                  v[b:b + 1, hq // g:hq // g + 1], do[b:b + 1, hq:hq + 1], w.scale, causal)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    t = time.perf_counter() - t0
+    fl = 2.5 * attn_flops(1, heads, w.Sq, w.Skv, w.D, causal)
+    return {"value": round(fl / t / 1e12, 6), "unit": "TFLOPS", "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": f"{heads} whole query heads of {w.name} (fp64 numpy backward oracle, {t:.1f} s on "
+                      f"{_cpu_model()})"}
 
 
 def bench_workload(args, w, make_inputs):
@@ -235,7 +292,14 @@ def bench_workload(args, w, make_inputs):
         "ms_p95": round(float(np.percentile(tl, 95)) * 1e3, 4), "ms_min": round(float(tl.min()) * 1e3, 4),
         "ms_loop100": round(t_loop * 1e3, 4), "tflops_loop100": round(flops / t_loop / 1e12, 2),
         "frac_of_peak": round(tf / PEAK_TFLOPS[dtn], 4), "key_splits": nsplit if nsplit is not None else 1,
-        "workgroups": w.B * w.Hq * ((w.Sq + 255) // 256)}), flush=True)
+        "workgroups": w.B * w.Hq * ((w.Sq + 255) // 256),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS[dtn], "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_TFLOPS[dtn], 4), "traffic": None,
+                     "kernel": f"attn_fwd_kernel<{w.D},{str(causal).lower()},{str(dtn == 'fp8').lower()},"
+                               f"{str(local).lower()},*>" + (" + merge_splits_kernel" if nsplit is not None else ""),
+                     "mean_launch_ms": round(float(tl.mean()) * 1e3, 4)},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_workload(inp, w, causal, args.cpu_seconds)}),
+        flush=True)
 
 
 def bench_backward(args, w):
@@ -249,14 +313,16 @@ def bench_backward(args, w):
     dev = torch.device("cuda:0")
     base = 1000 * w.wid
 
-    def put(seed, shape):
-        a = to_bf16_bits(normal(shape, seed))
+    bits = {}
+
+    def put(name, seed, shape):
+        a = bits[name] = to_bf16_bits(normal(shape, seed))
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    Q = put(base + 0, (w.B, w.Hq, w.Sq, w.D))
-    K = put(base + 1, (w.B, w.Hkv, w.Skv, w.D))
-    V = put(base + 2, (w.B, w.Hkv, w.Skv, w.D))
-    dO = put(base + 3, (w.B, w.Hq, w.Sq, w.D))
+    Q = put("q", base + 0, (w.B, w.Hq, w.Sq, w.D))
+    K = put("k", base + 1, (w.B, w.Hkv, w.Skv, w.D))
+    V = put("v", base + 2, (w.B, w.Hkv, w.Skv, w.D))
+    dO = put("do", base + 3, (w.B, w.Hq, w.Sq, w.D))
     causal = bool(w.causal[-1])
     O, L = ha.forward(Q, K, V, scale=w.scale, causal=causal)
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
@@ -291,6 +357,11 @@ def bench_backward(args, w):
     t_loop = e0.elapsed_time(e1) * 1e-3 / 100
     flops = 2.5 * attn_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, causal)   # five products of 2*D flops per pair
     tf = flops / tl.mean() / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cpu = cpu_baseline_backward(*(oracle.dequantise(bits[n], "bf16", 1.0) for n in ("q", "k", "v", "do")),
+                                    w, causal, args.cpu_seconds)
     print(json.dumps({
         "metric": f"attn bwd TFLOPS (bf16) at {w.name}", "value": round(tf, 2), "unit": "TFLOPS",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
@@ -301,7 +372,13 @@ def bench_backward(args, w):
         "ms_mean": round(float(tl.mean()) * 1e3, 4), "ms_p50": round(float(np.median(tl)) * 1e3, 4),
         "ms_p95": round(float(np.percentile(tl, 95)) * 1e3, 4), "ms_min": round(float(tl.min()) * 1e3, 4),
         "ms_loop100": round(t_loop * 1e3, 4), "tflops_loop100": round(flops / t_loop / 1e12, 2),
-        "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "workspace_bytes": need}), flush=True)
+        "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4), "workspace_bytes": need,
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_TFLOPS["bf16"], 4), "traffic": None,
+                     "kernel": f"attn_bwd: attn_bwd_dq_kernel<{w.D},{str(causal).lower()}> + "
+                               f"attn_bwd_dkdv_kernel<{w.D},{str(causal).lower()}> (+ attn_bwd_group_sum_kernel)",
+                     "mean_launch_ms": round(float(tl.mean()) * 1e3, 4)},
+        "cpu_baseline": cpu}), flush=True)
 
 
 SWEEP_FWD = [  # B, H, S, D, causal, dtype
