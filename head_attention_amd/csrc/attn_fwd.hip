@@ -133,6 +133,8 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   constexpr int NDB = D / 32;                       // 32-wide output column blocks
   constexpr int NKB = kBN / 32;                     // 32-key blocks per tile
   constexpr float kPre = FP8 ? 4.f : 0.f;           // fp8: p carries a factor 2^kPre
+  // The software-pipelined tile loop (fp8 head dim 128 without a window).
+  constexpr bool PIPE = FP8 && !WIN && D == 128 && T::NINSTR % NW == 0;
   __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * 2 * T::BYTES];  // [slot][K, V]
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
 
@@ -182,6 +184,10 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     c *= qd * kd;
     oscale = vd;
   }
+  // c is negative only through an fp8 descale of that sign; then the largest
+  // c*s belongs to the smallest s, and a masked key holds +inf (c*s = -inf).
+  const bool cneg = FP8 && c < 0.f;
+  const float smask = cneg ? INFINITY : -INFINITY;
 
   // Key tiles this workgroup needs, and those this wave needs.
   const int rows_end = min(q0 + kRows, p.Sq);
@@ -277,6 +283,11 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   // one fp32 ulp of l, and over 10^5 tiles those roundings would bias l.
   float m = -INFINITY;
   double l = 0.0;
+  // bf16: dl gathers sum(bf16(p) - p), so that l + dl is the sum of the very
+  // P values the P V product consumes. O is divided by that sum: a key that
+  // carries most of a row's weight then cancels exactly, whatever the rounding
+  // of its p. The LSE keeps the unrounded l.
+  [[maybe_unused]] float dl = 0.f;
 
   // Per-lane constant parts of the LDS operand addresses.
   // K operand (A of S^T): row 32*kb + n, logical chunk per dc.
@@ -288,9 +299,11 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   // own copies of tile t (the copies of later tiles may still be in flight),
   // then the barrier publishes tile t and retires slot (t-1) % kStages, which
   // is refilled with tile t + kStages - 1.
+  if constexpr (!PIPE) {
 #pragma unroll
-  for (int u = 0; u < kStages - 1; ++u)
-    if (u < ntot) issue(u);
+    for (int u = 0; u < kStages - 1; ++u)
+      if (u < ntot) issue(u);
+  }
   // Tile u of the sequence: wait for this wave's copies of it, barrier, queue
   // tile u + kStages - 1 into the slot every wave is done with.
   auto sync = [&](int u) __attribute__((always_inline)) {
@@ -351,7 +364,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
           const int kp = key + kv_start;
           bool ok = key < Skv && (!CAUSAL || kp <= qi);
           if constexpr (WIN) ok = ok && ((kp >= qi - wl && kp <= qi + wr) || kp < sink);
-          s[kb][i] = ok ? s[kb][i] : -INFINITY;
+          s[kb][i] = ok ? s[kb][i] : smask;
         }
     }
 
@@ -374,14 +387,22 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
         rs += pv;
       }
     if (__any(m == -INFINITY || !(rs <= 256.f))) {
-      float mx = -INFINITY;
+      float mx = -INFINITY;   // max of s, or of -s when c < 0
+      if (!cneg) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sraw[kb][i]);
-      const float mnew = fmaxf(m, xor32_max(mx) * c);
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sraw[kb][i]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, -sraw[kb][i]);
+      }
+      const float mnew = fmaxf(m, xor32_max(mx) * fabsf(c));
       const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 when m was -inf
       l *= (double)alpha;
+      if constexpr (!FP8) dl *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
       m = mnew;
@@ -401,6 +422,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     // ---- O^T += V^T P^T ----
     if constexpr (!FP8) {
       const int rr = l16 >> 2, ss = l16 & 3;
+      float dr = -rs;   // becomes sum(bf16(p)) - sum(p) over this tile
 #pragma unroll
       for (int kg = 0; kg < kBN / 16; ++kg) {  // 16-key groups
         const int kb = kg >> 1, half = kg & 1;
@@ -411,6 +433,8 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
                                  pack_bf16(s[kb][8 * half + 4], s[kb][8 * half + 5]),
                                  pack_bf16(s[kb][8 * half + 6], s[kb][8 * half + 7])};
           pf = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) dr = sum_bf16x2(pk[w], dr);
         }
         const int key1 = 32 * kb + 16 * half + 4 * g + rr;   // keys key1, key1+8
 #pragma unroll
@@ -425,6 +449,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[db], 0, 0, 0);
         }
       }
+      dl += dr;
     } else {
       const int rr = l16 >> 1, hh = l16 & 1;
 #pragma unroll
@@ -460,7 +485,251 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       }
     }
   };
-  if constexpr (!WIN) {
+  if constexpr (PIPE) {
+    // ---- software-pipelined tile loop ----
+    // Iteration u (0 .. ntot) runs S(u+1) = K(u+1) Q^T and O += V(u-1)^T
+    // P(u-1) on the MFMAs while the VALU turns S(u) into P(u): the three are
+    // independent, so the wave's softmax instructions issue between its MFMAs
+    // instead of after them. K(x) is copied into K slot x % 4 four iterations
+    // before it is read and V(x) into V slot x % 4 two iterations before, so
+    // that a slot is refilled only after every wave has read it and each copy
+    // has three iterations to land. S and P are double buffered: S(u) lives in
+    // S[u & 1], P(u) in P[u & 1].
+    static_assert(kStages == 4, "the pipelined loop assumes rings of four slots");
+    constexpr int PWK = T::NINSTR / kW;   // K pieces (and V pieces) per wave per tile
+    int gk[PWK], gv[PWK];
+    unsigned lk[PWK];
+#pragma unroll
+    for (int j = 0; j < PWK; ++j) {
+      const int c0 = (wv * PWK + j) * 64, cidx = c0 + lane, r = cidx / T::CH, pc = cidx % T::CH;
+      gk[j] = r * ROWB + ((pc ^ T::kswz(r)) * 16);
+      gv[j] = r * ROWB + ((pc ^ T::vswz(r)) * 16);
+      lk[j] = __builtin_amdgcn_readfirstlane(smem_addr + c0 * 16);
+    }
+    auto issue_k = [&](int t, int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < PWK; ++j) dma16(rkw, t * (kBN * ROWB) + gk[j], lk[j] + slot * (2 * T::BYTES));
+    };
+    auto issue_v = [&](int t, int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < PWK; ++j) dma16(rvw, t * (kBN * ROWB) + gv[j], lk[j] + slot * (2 * T::BYTES) + T::BYTES);
+    };
+    // Iteration u needs K(u+1) and V(u-1), both copied in iteration u-3; the
+    // copies of iterations u-2 and u-1 may still be in flight. After the
+    // barrier, K(u+4) and V(u+2) are queued into the slots of K(u) and V(u-2).
+    auto psync = [&](int u) __attribute__((always_inline)) {
+      const int r = ntot - u;
+      if (r >= 4) wait_vmcnt<4 * PWK>();
+      else if (r == 3) wait_vmcnt<3 * PWK>();
+      else if (r == 2) wait_vmcnt<2 * PWK>();
+      else if (r == 1) wait_vmcnt<PWK>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (u + 4 < ntot) issue_k(u + 4, u & 3);
+      if (u + 2 < ntot) issue_v(u + 2, (u + 2) & 3);
+    };
+
+    // Per-lane LDS operand offsets. K: row n (rows 32 apart share the swizzle),
+    // 16-byte chunk 4 dc + 2 g + h. V (transposing reads): key kv0 + 16 i for
+    // i = 0..3 (keys 16 apart share the swizzle), chunk 2 db + dgrp.
+    int koff[D / 64][2];
+#pragma unroll
+    for (int dc = 0; dc < D / 64; ++dc)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) koff[dc][h] = krow * ROWB + (((4 * dc + 2 * g + h) ^ T::kswz(krow)) * 16);
+    const int rr = l16 >> 1, hh = l16 & 1;
+    const int kv0 = 8 * (rr >> 2) + 4 * g + (rr & 3);
+    int voff[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) voff[db] = kv0 * ROWB + (((2 * db + dgrp) ^ T::vswz(kv0)) * 16) + 8 * hh;
+
+    f32x16 S[2][NKB];
+    int P[2][8];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) P[b][w] = 0;
+
+    auto kload = [&](int slot, int kb, int dc) __attribute__((always_inline)) {
+      const LDS_AS char* kp = smem + slot * (2 * T::BYTES) + kb * 32 * ROWB;
+      const i32x4 k0 = *(const LDS_AS i32x4*)(kp + koff[dc][0]);
+      const i32x4 k1 = *(const LDS_AS i32x4*)(kp + koff[dc][1]);
+      return i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+    };
+    auto vload = [&](int slot, int db) __attribute__((always_inline)) {
+      const LDS_AS char* vp = smem + slot * (2 * T::BYTES) + T::BYTES + voff[db];
+      int vw[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(vp + i * 16 * ROWB));
+        vw[2 * i] = x[0];
+        vw[2 * i + 1] = x[1];
+      }
+      return i32x8{vw[0], vw[1], vw[2], vw[3], vw[4], vw[5], vw[6], vw[7]};
+    };
+    auto mfma8 = [](i32x8 a, i32x8 b, f32x16 c) __attribute__((always_inline)) {
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    };
+    auto pfrag = [](const int (&pw)[8]) __attribute__((always_inline)) {
+      return i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+    };
+    // S(next) = K Q^T and O += V^T P(prev), MFMAs alternating between the two
+    // products; do_qk / do_pv drop either (edge iterations).
+    auto mma = [&](f32x16 (&sn)[NKB], const int (&pp)[8], int kslot, int vslot, bool do_qk, bool do_pv)
+        __attribute__((always_inline)) {
+      static_assert(NKB == 2 && D / 64 == 2 && NDB == 4, "fp8 hd128 tile shapes");
+      const i32x8 pf = pfrag(pp);
+      if (do_qk) { sn[0] = f32x16{}; sn[1] = f32x16{}; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kb = i & 1, dc = i >> 1;
+        if (do_qk) sn[kb] = mfma8(kload(kslot, kb, dc), qf8[dc], sn[kb]);
+        if (do_pv) o[i] = mfma8(vload(vslot, i), pf, o[i]);
+      }
+    };
+    // Softmax of one tile: P (e4m3fn, scaled by 2^kPre) from S, with the
+    // checked running max; the pack happens before the check and is redone if
+    // the tile re-bases.
+    // keep(): called on the rare re-base path only; the steady loop passes one
+    // that uses the next tile's scores there, which keeps their MFMAs ahead of
+    // the branch (inside the interleaved region) instead of sunk past it.
+    auto softmax = [&](f32x16 (&sc)[NKB], int (&pw)[8], auto masked_c, int t, auto sched_c, auto keep)
+        __attribute__((always_inline)) {
+      if constexpr (decltype(masked_c)::value) {
+        const int key0 = t * kBN;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+            const bool ok = key < Skv && (!CAUSAL || key + kv_start <= qi);
+            sc[kb][i] = ok ? sc[kb][i] : smask;
+          }
+      }
+      auto expo = [&](float moff, float& rs) __attribute__((always_inline)) {
+        float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int kb = w >> 2, i = 4 * (w & 3);
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 0], c, moff));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, moff));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 2], c, moff));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 3], c, moff));
+          if (kb == 0) r0 += (p0 + p1) + (p2 + p3);
+          else r1 += (p0 + p1) + (p2 + p3);
+          // the first conversion writes the low half-word only; the word of two
+          // tiles back is passed as the kept half so that nothing is cleared
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[w], false);
+          pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
+        }
+        rs = r0 + r1;
+      };
+      float moff = kPre - (m == -INFINITY ? 0.f : m);
+      float rs;
+      expo(moff, rs);
+      if constexpr (decltype(sched_c)::value) {
+        // Interleave: the eight MFMAs of mma() one by one, each followed by its
+        // share of the softmax VALU work and the LDS operand reads of the MFMA
+        // two places later.
+#define HAT_SLOT(nds)                                    \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     \
+  __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);   \
+  __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        HAT_SLOT(2) HAT_SLOT(4) HAT_SLOT(2) HAT_SLOT(4) HAT_SLOT(2) HAT_SLOT(4) HAT_SLOT(0) HAT_SLOT(0)
+#undef HAT_SLOT
+      }
+      if (__any(m == -INFINITY || !(rs <= 256.f))) {
+        keep();
+        // the scores pass through an empty asm here, so that the row max below
+        // cannot be speculated ahead of the branch into the common path
+        asm volatile("" : "+v"(sc[0]), "+v"(sc[1]));
+        float mx = -INFINITY;   // max of s, or of -s when c < 0
+        if (!cneg) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, -sc[kb][i]);
+        }
+        const float mnew = fmaxf(m, xor32_max(mx) * fabsf(c));
+        const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 when m was -inf
+        l *= (double)alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        m = mnew;
+        moff = kPre - (m == -INFINITY ? 0.f : m);
+        expo(moff, rs);
+      }
+      l += (double)rs;
+    };
+
+    // The wave's bounds, made provably wave-uniform so that the loops below
+    // branch on scalars: its tile count, its first masked tile, and the end
+    // of its steady iterations (1 .. ss_end-1 run every part unmasked).
+    const int w_nt = __builtin_amdgcn_readfirstlane(w_ntiles);
+    const int w_fm = __builtin_amdgcn_readfirstlane(CAUSAL ? min(Skv / kBN, max(0, qw - kv_start + 1) / kBN)
+                                                           : Skv / kBN);
+    const int ss_end = min(w_nt - 1, w_fm);
+    // One iteration with its parts decided at run time (the edges of the loop).
+    auto edge = [&](int u, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], int (&pc)[8], const int (&pp)[8])
+        __attribute__((always_inline)) {
+      psync(u);
+      mma(sn, pp, (u + 1) & 3, (u + 3) & 3, u + 1 < w_nt, u >= 1 && u <= w_nt);
+      __builtin_amdgcn_sched_barrier(0);   // edges are rare: not interleaved, fewer live registers
+      auto none = []() __attribute__((always_inline)) {};
+      if (u < w_nt) {
+        if (u >= w_fm) softmax(sc, pc, std::true_type{}, u, std::false_type{}, none);
+        else softmax(sc, pc, std::false_type{}, u, std::false_type{}, none);
+      }
+    };
+    // A steady iteration: every part runs, unmasked, interleaved.
+    auto steady = [&](int u, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], int (&pc)[8], const int (&pp)[8], int kslot,
+                      int vslot) __attribute__((always_inline)) {
+      psync(u);
+      mma(sn, pp, kslot, vslot, true, true);
+      auto keep = [&]() __attribute__((always_inline)) { asm volatile("" ::"v"(sn[0]), "v"(sn[1])); };
+      softmax(sc, pc, std::false_type{}, u, std::true_type{}, keep);
+    };
+
+    // Prologue: K(0..3) and V(0..1) in the order of the iterations that
+    // would have queued them; wait for K(0), then S(0).
+    if (ntot > 0) issue_k(0, 0);
+    if (ntot > 1) issue_k(1, 1);
+    if (ntot > 2) issue_k(2, 2);
+    if (ntot > 0) issue_v(0, 0);
+    if (ntot > 3) issue_k(3, 3);
+    if (ntot > 1) issue_v(1, 1);
+    if (ntot >= 4) wait_vmcnt<5 * PWK>();
+    else if (ntot == 3) wait_vmcnt<4 * PWK>();
+    else if (ntot == 2) wait_vmcnt<3 * PWK>();
+    else wait_vmcnt<PWK>();
+    __syncthreads();
+    if (w_nt > 0) mma(S[0], P[1], 0, 0, true, false);
+    if (ntot > 0) {
+      edge(0, S[0], S[1], P[0], P[1]);
+      int u = 1;
+      // Steady iterations four at a time (u = 1 mod 4 at the top), so that the
+      // ring slots and buffers are compile-time constants.
+      for (; u + 3 < ss_end; u += 4) {
+        steady(u + 0, S[1], S[0], P[1], P[0], 2, 0);
+        steady(u + 1, S[0], S[1], P[0], P[1], 3, 1);
+        steady(u + 2, S[1], S[0], P[1], P[0], 0, 2);
+        steady(u + 3, S[0], S[1], P[0], P[1], 1, 3);
+      }
+      // The rest (u is odd here), two at a time with compile-time buffers.
+      for (; u <= ntot; u += 2) {
+        edge(u, S[1], S[0], P[1], P[0]);
+        if (u + 1 > ntot) break;
+        edge(u + 1, S[0], S[1], P[0], P[1]);
+      }
+    }
+  } else if constexpr (!WIN) {
     const int first_masked = CAUSAL ? min(Skv / kBN, max(0, qw - kv_start + 1) / kBN) : Skv / kBN;
     const int n_plain = min(first_masked, ntot);
     int u = 0;
@@ -556,7 +825,8 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   if (!wave_live) return;
   const int qi_full = qi;
   const float ltot = xor32_sum((float)l);
-  const float inv = ltot > 0.f ? oscale / ltot : 0.f;
+  const float lp = FP8 ? ltot : xor32_sum((float)l + dl);   // sum of the P the MFMAs consumed
+  const float inv = ltot > 0.f ? oscale / lp : 0.f;
   const float lse = ltot > 0.f ? (m + __log2f(ltot) - kPre) * 0.69314718055994531f : -INFINITY;
   if (p.o32 == nullptr || split < 0) {
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + qrow0 * (size_t)(D * 2), (uint32_t)p.Sq * D * 2);

@@ -38,10 +38,14 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
 // [lds_base + 16 l, +16) from buffer offset voff (out-of-range offsets read as
 // zero). Written as asm so that the compiler does not make later LDS reads of
 // other ring slots wait for it; the kernel waits on vmcnt itself before the
-// barrier that publishes a slot.
+// barrier that publishes a slot. The copy takes its LDS address from m0, a
+// register the compiler reserves: the asm saves m0 and puts it back once the
+// load has been issued (the load reads m0 at issue).
 __device__ __forceinline__ void dma16(const i32x4 rsrc, int voff, unsigned lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(lds_base) : "memory");
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(rsrc), "s"(lds_base) : "memory");
 }
 
 template <int N>
@@ -57,6 +61,12 @@ __device__ __forceinline__ float xor32_max(float x) {
 __device__ __forceinline__ float xor32_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// acc + lo + hi of a packed bf16 pair (dot product with (1, 1), fp32 accumulate).
+__device__ __forceinline__ float sum_bf16x2(unsigned pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                         acc, false);
 }
 
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {

@@ -82,7 +82,12 @@ typedef enum {
  *   scale        softmax scale (finite, > 0), e.g. 1/sqrt(D).
  *   causal       nonzero: key j is allowed for query i iff j <= i (top-left).
  *   q/k/v_descale  fp8 only: device pointers to one fp32 each; NULL means 1.
- *                Ignored for bf16.
+ *                Ignored for bf16. Read on the device, so the host cannot check
+ *                them: any finite value is accepted, of either sign (a negative
+ *                q_descale * k_descale makes the largest score the one of the
+ *                smallest code product, and the kernel takes its row max that
+ *                way); a NaN or infinite descale gives NaN or infinite out and
+ *                lse.
  *   stream       hipStream_t to enqueue on.
  *
  * A row with no allowed key gets O = 0 and LSE = -inf.
@@ -130,7 +135,11 @@ attn_status_t attn_fwd_window(const void* q, const void* k, const void* v, void*
                               void* stream);
 
 /*
- * attn_merge_lse2_host — merge two partial results on the HOST.
+ * attn_merge_lse2_host — merge two partial results on the HOST: the out/LSE
+ * combination of attention over two key chunks that the page "feat(attention):
+ * add strict bitwise ROCm path" performs across context-parallel ranks (Summary
+ * table: the boundary returns (out, lse); Q/K/V all-gather then Out/LSE
+ * reduce-scatter), here as a plain host routine run after the two chunk calls.
  *
  *   o1, o2, o_out  host bf16 bit patterns [B, H, S, D]
  *   lse1, lse2, lse_out  host fp32 [B, H, S] (natural log)
@@ -258,7 +267,10 @@ attn_status_t attn_bwd_chunk(const void* q, const void* k, const void* v, const 
  * heads are split over workgroups; -1 on invalid arguments. */
 int64_t attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D);
 
-/* Static, human-readable name of a status code (never NULL). */
+/* Static, human-readable name of a status code (never NULL). Every entry point
+ * fails closed with one of these codes rather than falling back to another
+ * path, the refusal the page "feat(attention): add strict bitwise ROCm path"
+ * asks of an unsupported request (Summary and Changes sections). */
 const char* attn_status_string(attn_status_t s);
 
 #ifdef __cplusplus

@@ -76,10 +76,12 @@ def test_random_forward(c):
     if fmt == "bf16":
         check_bf16(O, L, Oref, Lref, what=fmt_case(c))
     else:
+        Aref, _ = oracle.attention_forward(q, k, np.abs(v), scale, c["causal"], c["kv_start"],
+                                           window_left=c["wl"], window_right=c["wr"], sink=c["sink"])
         live = ~np.isneginf(Lref)
         assert np.array_equal(np.isneginf(L), ~live) and (O[~live] == 0).all()
         if live.any():
-            check_fp8(O[live], L[live], Oref[live], Lref[live], what=fmt_case(c))
+            check_fp8(O[live], L[live], Oref[live], Lref[live], Aref[live], what=fmt_case(c))
 
 
 def draw_backward(i):

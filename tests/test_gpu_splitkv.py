@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import head_attention_amd as ha
-from gpu_helpers import say, oracle_ref, synth_inputs, check_bf16, check_fp8, to_dev, descale_dev, make_inputs, WORKLOADS
+from gpu_helpers import say, oracle_ref, refs, check_any, synth_inputs, check_bf16, check_fp8, to_dev, descale_dev, make_inputs, WORKLOADS
 
 pytestmark = pytest.mark.gpu
 
@@ -52,13 +52,13 @@ def test_splitkv_matches_oracle_and_unsplit(case):
     inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, fmt, seed=3 + Sq + Skv + ns)
     scale = 1 / math.sqrt(D)
     O, L, Ou, Lu = run_split(inp, scale, causal, ns)
-    Oref, Lref = oracle_ref(inp, scale, causal)
+    R = refs(inp, scale, causal)
     if fmt == "bf16":
-        check_bf16(O, L, Oref, Lref, what=f"split {case}")
+        check_any(inp, O, L, R, what=f"split {case}")
     else:
-        live = ~np.isneginf(Lref)
+        live = ~np.isneginf(R[1])
         assert np.array_equal(np.isneginf(L), ~live) and (O[~live] == 0).all()
-        check_fp8(O[live], L[live], Oref[live], Lref[live], what=f"split {case}")
+        check_any(inp, O, L, R, what=f"split {case}", live=live)
     # against the unsplit kernel: only fp32 rounding of the partials separates them
     fin = np.isfinite(Lu)
     assert np.array_equal(np.isfinite(L), fin)
@@ -93,11 +93,7 @@ def test_splitkv_library_choice(case):
     inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, fmt, seed=11 + Sq + Skv)
     scale = 1 / math.sqrt(D)
     O, L, Ou, Lu = run_split(inp, scale, causal, 0, workspace=ws)
-    Oref, Lref = oracle_ref(inp, scale, causal)
-    if fmt == "bf16":
-        check_bf16(O, L, Oref, Lref, what=f"library choice {case}")
-    else:
-        check_fp8(O, L, Oref, Lref, what=f"library choice {case}")
+    check_any(inp, O, L, refs(inp, scale, causal), what=f"library choice {case}")
     fin = np.isfinite(Lu)
     assert np.array_equal(np.isfinite(L), fin)
     if causal and B * Hq * ((Sq + 255) // 256) >= 256:
@@ -146,11 +142,7 @@ def test_splitkv_tail_only_split(fmt):
     inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, fmt, seed=77)
     scale = 1 / math.sqrt(D)
     O, L, Ou, Lu = run_split(inp, scale, False, 0)
-    Oref, Lref = oracle_ref(inp, scale, False)
-    if fmt == "bf16":
-        check_bf16(O, L, Oref, Lref, what="tail split")
-    else:
-        check_fp8(O, L, Oref, Lref, what="tail split")
+    check_any(inp, O, L, refs(inp, scale, False), what="tail split")
     # rows of whole tiles are the unsplit kernel's bits; tail rows agree to fp32 rounding
     whole_rows = (256 // 7) * Sq + (256 % 7) * 256          # first row of the first tail tile
     flatO, flatOu = O.reshape(-1, D), Ou.reshape(-1, D)

@@ -31,23 +31,23 @@ def run_window(inp, scale, causal, wl, wr, sink, kv_start=0):
     return O.float().cpu().numpy(), L.cpu().numpy()
 
 
-def oracle_window(inp, scale, causal, wl, wr, sink, kv_start=0, rows=None):
+def oracle_window(inp, scale, causal, wl, wr, sink, kv_start=0, rows=None, abs_v=False):
     fmt = inp["fmt"]
     q = oracle.dequantise(inp["q"], fmt, inp["q_descale"])
     k = oracle.dequantise(inp["k"], fmt, inp["k_descale"])
     v = oracle.dequantise(inp["v"], fmt, inp["v_descale"])
-    return oracle.attention_forward(q, k, v, scale, causal, kv_start, rows=rows,
+    return oracle.attention_forward(q, k, np.abs(v) if abs_v else v, scale, causal, kv_start, rows=rows,
                                     window_left=wl, window_right=wr, sink=sink)
 
 
-def check(inp, O, L, Oref, Lref, what):
+def check(inp, O, L, Oref, Lref, what, Aref=None):
     if inp["fmt"] == "bf16":
         check_bf16(O, L, Oref, Lref, what=what)
     else:
         live = ~np.isneginf(Lref)
         assert np.array_equal(np.isneginf(L), ~live), f"{what}: -inf LSE rows differ"
         assert (O[~live] == 0).all()
-        check_fp8(O[live], L[live], Oref[live], Lref[live], what=what)
+        check_fp8(O[live], L[live], Oref[live], Lref[live], Aref[live] if Aref is not None else None, what=what)
 
 
 CASES = [
@@ -75,7 +75,8 @@ def test_window_matches_oracle(case):
     scale = 1 / math.sqrt(D)
     O, L = run_window(inp, scale, causal, wl, wr, sink, ks)
     Oref, Lref = oracle_window(inp, scale, causal, wl, wr, sink, ks)
-    check(inp, O, L, Oref, Lref, what=f"window {case}")
+    Aref = oracle_window(inp, scale, causal, wl, wr, sink, ks, abs_v=True)[0] if inp["fmt"] != "bf16" else None
+    check(inp, O, L, Oref, Lref, what=f"window {case}", Aref=Aref)
 
 
 def test_zero_width_window_returns_own_value_row():
