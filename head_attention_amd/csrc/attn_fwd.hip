@@ -133,9 +133,12 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   constexpr int NDB = D / 32;                       // 32-wide output column blocks
   constexpr int NKB = kBN / 32;                     // 32-key blocks per tile
   constexpr float kPre = FP8 ? 4.f : 0.f;           // fp8: p carries a factor 2^kPre
-  // The software-pipelined tile loop (fp8 head dim 128 without a window).
+  // The software-pipelined tile loop (fp8 head dim 128 without a window)
+  // synchronises every kSync tiles, over rings of 2 kSync slots for K and V.
   constexpr bool PIPE = FP8 && !WIN && D == 128 && T::NINSTR % NW == 0;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * 2 * T::BYTES];  // [slot][K, V]
+  constexpr int kSync = 4;
+  constexpr int kLds = PIPE ? 2 * (2 * kSync) * T::BYTES : kStages * 2 * T::BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kLds];  // PIPE: [K ring][V ring]; else [slot][K, V]
   LDS_AS char* smem = (LDS_AS char*)smem_raw;
 
   const int BH = p.B * p.Hq;
@@ -151,8 +154,18 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     }
   } else {
     const int per_split = BH * p.n_qtiles;
-    split = (int)(blockIdx.x / per_split);
-    bid = (int)(blockIdx.x % per_split);
+    int gb = (int)blockIdx.x;
+    if constexpr (!CAUSAL) {
+      // Workgroups go to the eight XCDs round-robin (workgroup i to XCD i % 8)
+      // and each XCD has an L2 of its own: give XCD x one contiguous range of
+      // the grid's work instead, so that the workgroups an XCD runs at a time
+      // share their key/value head. (Causal grids keep their longest-first
+      // order, which balances them.)
+      const int n = (int)gridDim.x, q8 = n >> 3, rem = n & 7, x = gb & 7, r = gb >> 3;
+      gb = x < rem ? x * (q8 + 1) + r : rem * (q8 + 1) + (x - rem) * q8 + r;
+    }
+    split = gb / per_split;
+    bid = gb % per_split;
   }
   int bh, qt;
   if (CAUSAL) {  // longest rows first
@@ -490,12 +503,14 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     // Iteration u (0 .. ntot) runs S(u+1) = K(u+1) Q^T and O += V(u-1)^T
     // P(u-1) on the MFMAs while the VALU turns S(u) into P(u): the three are
     // independent, so the wave's softmax instructions issue between its MFMAs
-    // instead of after them. K(x) is copied into K slot x % 4 four iterations
-    // before it is read and V(x) into V slot x % 4 two iterations before, so
-    // that a slot is refilled only after every wave has read it and each copy
-    // has three iterations to land. S and P are double buffered: S(u) lives in
-    // S[u & 1], P(u) in P[u & 1].
-    static_assert(kStages == 4, "the pipelined loop assumes rings of four slots");
+    // instead of after them. K(x) lives in K slot x % NS and V(x) in V slot
+    // x % NS (NS = 2 kSync); the workgroup synchronises every kSync
+    // iterations (one barrier per kSync * 64 keys), queueing K kSync+1 to
+    // 2 kSync tiles and V kSync-1 to 2 kSync-2 tiles ahead, so that a slot is
+    // refilled only after every wave has read it. S and P are double
+    // buffered: S(u) lives in S[u & 1], P(u) in P[u & 1].
+    constexpr int NS = 2 * kSync;
+    static_assert(NS == 8, "the steady loop below is unrolled over eight ring slots");
     constexpr int PWK = T::NINSTR / kW;   // K pieces (and V pieces) per wave per tile
     int gk[PWK], gv[PWK];
     unsigned lk[PWK];
@@ -506,58 +521,90 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       gv[j] = r * ROWB + ((pc ^ T::vswz(r)) * 16);
       lk[j] = __builtin_amdgcn_readfirstlane(smem_addr + c0 * 16);
     }
+    // LDS: the K ring (kStages tiles) and then the V ring, so that every slot
+    // of either ring lies within the reads' 16-bit immediate offsets.
+    constexpr int KRING = 0, VRING = NS * T::BYTES;
     auto issue_k = [&](int t, int slot) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < PWK; ++j) dma16(rkw, t * (kBN * ROWB) + gk[j], lk[j] + slot * (2 * T::BYTES));
+      for (int j = 0; j < PWK; ++j) dma16(rkw, t * (kBN * ROWB) + gk[j], lk[j] + KRING + slot * T::BYTES);
     };
     auto issue_v = [&](int t, int slot) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < PWK; ++j) dma16(rvw, t * (kBN * ROWB) + gv[j], lk[j] + slot * (2 * T::BYTES) + T::BYTES);
+      for (int j = 0; j < PWK; ++j) dma16(rvw, t * (kBN * ROWB) + gv[j], lk[j] + VRING + slot * T::BYTES);
     };
-    // Iteration u needs K(u+1) and V(u-1), both copied in iteration u-3; the
-    // copies of iterations u-2 and u-1 may still be in flight. After the
-    // barrier, K(u+4) and V(u+2) are queued into the slots of K(u) and V(u-2).
+    // Iteration u = kSync U synchronises: each wave waits for its own copies
+    // (those queued kSync iterations earlier; nothing else is in flight then),
+    // and the barrier publishes them and retires every slot read in
+    // iterations u-kSync .. u-1; then K(u+kSync+1 .. u+2kSync) and
+    // V(u+kSync-1 .. u+2kSync-2) are queued for the next kSync iterations.
+    // Iterations u .. u+kSync-1 read K(u+1 .. u+kSync) and V(u-1 ..
+    // u+kSync-2), all published at u.
     auto psync = [&](int u) __attribute__((always_inline)) {
-      const int r = ntot - u;
-      if (r >= 4) wait_vmcnt<4 * PWK>();
-      else if (r == 3) wait_vmcnt<3 * PWK>();
-      else if (r == 2) wait_vmcnt<2 * PWK>();
-      else if (r == 1) wait_vmcnt<PWK>();
-      else wait_vmcnt<0>();
+      wait_vmcnt<0>();
       __syncthreads();
-      if (u + 4 < ntot) issue_k(u + 4, u & 3);
-      if (u + 2 < ntot) issue_v(u + 2, (u + 2) & 3);
+#pragma unroll
+      for (int j = 1; j <= kSync; ++j)
+        if (u + kSync + j < ntot) issue_k(u + kSync + j, (u + kSync + j) % NS);
+#pragma unroll
+      for (int j = 0; j < kSync; ++j)
+        if (u + kSync - 1 + j < ntot) issue_v(u + kSync - 1 + j, (u + kSync - 1 + j) % NS);
     };
 
-    // Per-lane LDS operand offsets. K: row n (rows 32 apart share the swizzle),
-    // 16-byte chunk 4 dc + 2 g + h. V (transposing reads): key kv0 + 16 i for
-    // i = 0..3 (keys 16 apart share the swizzle), chunk 2 db + dgrp.
-    int koff[D / 64][2];
-#pragma unroll
-    for (int dc = 0; dc < D / 64; ++dc)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) koff[dc][h] = krow * ROWB + (((4 * dc + 2 * g + h) ^ T::kswz(krow)) * 16);
-    const int rr = l16 >> 1, hh = l16 & 1;
-    const int kv0 = 8 * (rr >> 2) + 4 * g + (rr & 3);
+    // Per-lane LDS operand offsets (rows 32 apart, and keys 16 apart, share
+    // the swizzle, so tiles and key groups add immediate offsets).
+    //  fp8:  K row n, 16-byte chunk 4 dc + 2 g + h; V (transposing reads) key
+    //        kv0 + 16 i for i = 0..3, chunk 2 db + dgrp.
+    //  bf16: K row n, chunk 2 dc + g; V keys kv0 + 16 kg and + 8, column
+    //        32 db + 16 dgrp + 4 ss.
+    constexpr int NKO = FP8 ? 2 * (D / 64) : D / 16;
+    int koff[NKO];
     int voff[NDB];
+    if constexpr (FP8) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) voff[db] = kv0 * ROWB + (((2 * db + dgrp) ^ T::vswz(kv0)) * 16) + 8 * hh;
+      for (int dc = 0; dc < D / 64; ++dc)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) koff[2 * dc + h] = krow * ROWB + (((4 * dc + 2 * g + h) ^ T::kswz(krow)) * 16);
+      const int rr = l16 >> 1, hh = l16 & 1;
+      const int kv0 = 8 * (rr >> 2) + 4 * g + (rr & 3);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) voff[db] = kv0 * ROWB + (((2 * db + dgrp) ^ T::vswz(kv0)) * 16) + 8 * hh;
+    } else {
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) koff[dc] = krow * ROWB + (((2 * dc + g) ^ T::kswz(krow)) * 16);
+      const int rr = l16 >> 2, ss = l16 & 3;
+      const int kv0 = 4 * g + rr;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = 32 * db + 16 * dgrp + 4 * ss;
+        voff[db] = kv0 * ROWB + (((col >> 3) ^ T::vswz(kv0)) * 16) + (col & 7) * 2;
+      }
+    }
 
+    // moff = kPre - m (kPre while m is -inf), changed only by a re-base; lf
+    // gathers the row-sum partials of up to four tiles in fp32 before they
+    // enter the fp64 l.
+    float moff = kPre;
+    float lf = 0.f;
+    auto flush = [&]() __attribute__((always_inline)) {
+      l += (double)lf;
+      lf = 0.f;
+    };
+    constexpr int NPW = FP8 ? 8 : 16;   // P words per lane and tile (e4m3fn x4 or bf16 x2)
     f32x16 S[2][NKB];
-    int P[2][8];
+    int P[2][NPW];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int w = 0; w < 8; ++w) P[b][w] = 0;
+      for (int w = 0; w < NPW; ++w) P[b][w] = 0;
 
-    auto kload = [&](int slot, int kb, int dc) __attribute__((always_inline)) {
-      const LDS_AS char* kp = smem + slot * (2 * T::BYTES) + kb * 32 * ROWB;
-      const i32x4 k0 = *(const LDS_AS i32x4*)(kp + koff[dc][0]);
-      const i32x4 k1 = *(const LDS_AS i32x4*)(kp + koff[dc][1]);
+    auto kload8 = [&](int slot, int kb, int dc) __attribute__((always_inline)) {
+      const LDS_AS char* kp = smem + KRING + slot * T::BYTES + kb * 32 * ROWB;
+      const i32x4 k0 = *(const LDS_AS i32x4*)(kp + koff[2 * dc]);
+      const i32x4 k1 = *(const LDS_AS i32x4*)(kp + koff[2 * dc + 1]);
       return i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
     };
-    auto vload = [&](int slot, int db) __attribute__((always_inline)) {
-      const LDS_AS char* vp = smem + slot * (2 * T::BYTES) + T::BYTES + voff[db];
+    auto vload8 = [&](int slot, int db) __attribute__((always_inline)) {
+      const LDS_AS char* vp = smem + VRING + slot * T::BYTES + voff[db];
       int vw[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -567,33 +614,53 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       }
       return i32x8{vw[0], vw[1], vw[2], vw[3], vw[4], vw[5], vw[6], vw[7]};
     };
+    auto kload16 = [&](int slot, int kb, int dc) __attribute__((always_inline)) {
+      return *(const LDS_AS bf16x8*)(smem + KRING + slot * T::BYTES + kb * 32 * ROWB + koff[dc]);
+    };
+    auto vload16 = [&](int slot, int kg, int db) __attribute__((always_inline)) {
+      const LDS_AS char* vp = smem + VRING + slot * T::BYTES + voff[db] + 16 * kg * ROWB;
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)vp);
+      const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + 8 * ROWB));
+      return __builtin_bit_cast(bf16x8, i16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]});
+    };
     auto mfma8 = [](i32x8 a, i32x8 b, f32x16 c) __attribute__((always_inline)) {
       return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
     };
-    auto pfrag = [](const int (&pw)[8]) __attribute__((always_inline)) {
-      return i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-    };
     // S(next) = K Q^T and O += V^T P(prev), MFMAs alternating between the two
     // products; do_qk / do_pv drop either (edge iterations).
-    auto mma = [&](f32x16 (&sn)[NKB], const int (&pp)[8], int kslot, int vslot, bool do_qk, bool do_pv)
+    auto mma = [&](f32x16 (&sn)[NKB], const int (&pp)[NPW], int kslot, int vslot, bool do_qk, bool do_pv)
         __attribute__((always_inline)) {
-      static_assert(NKB == 2 && D / 64 == 2 && NDB == 4, "fp8 hd128 tile shapes");
-      const i32x8 pf = pfrag(pp);
+      static_assert(NKB == 2 && NDB == 4, "hd128 tile shapes");
       if (do_qk) { sn[0] = f32x16{}; sn[1] = f32x16{}; }
+      if constexpr (FP8) {
+        const i32x8 pf = i32x8{pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kb = i & 1, dc = i >> 1;
-        if (do_qk) sn[kb] = mfma8(kload(kslot, kb, dc), qf8[dc], sn[kb]);
-        if (do_pv) o[i] = mfma8(vload(vslot, i), pf, o[i]);
+        for (int i = 0; i < 4; ++i) {
+          const int kb = i & 1, dc = i >> 1;
+          if (do_qk) sn[kb] = mfma8(kload8(kslot, kb, dc), qf8[dc], sn[kb]);
+          if (do_pv) o[i] = mfma8(vload8(vslot, i), pf, o[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kb = i & 1, dc = i >> 1, kg = i >> 2, db = i & 3;
+          if (do_qk) sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kload16(kslot, kb, dc), qf16[dc], sn[kb], 0, 0, 0);
+          if (do_pv) {
+            const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{(unsigned)pp[4 * kg], (unsigned)pp[4 * kg + 1],
+                                                                (unsigned)pp[4 * kg + 2], (unsigned)pp[4 * kg + 3]});
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vload16(vslot, kg, db), pf, o[db], 0, 0, 0);
+          }
+        }
       }
     };
-    // Softmax of one tile: P (e4m3fn, scaled by 2^kPre) from S, with the
-    // checked running max; the pack happens before the check and is redone if
-    // the tile re-bases.
+    // Softmax of one tile: P from S (e4m3fn scaled by 2^kPre, or bf16), with
+    // the checked running max; the pack happens before the check and is
+    // redone if the tile re-bases. bf16 also sums the rounded P (dot2 with
+    // (1, 1)) for the normalisation of O.
     // keep(): called on the rare re-base path only; the steady loop passes one
     // that uses the next tile's scores there, which keeps their MFMAs ahead of
     // the branch (inside the interleaved region) instead of sunk past it.
-    auto softmax = [&](f32x16 (&sc)[NKB], int (&pw)[8], auto masked_c, int t, auto sched_c, auto keep)
+    auto softmax = [&](f32x16 (&sc)[NKB], int (&pw)[NPW], auto masked_c, int t, auto sched_c, auto keep)
         __attribute__((always_inline)) {
       if constexpr (decltype(masked_c)::value) {
         const int key0 = t * kBN;
@@ -606,41 +673,75 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
             sc[kb][i] = ok ? sc[kb][i] : smask;
           }
       }
-      auto expo = [&](float moff, float& rs) __attribute__((always_inline)) {
-        float r0 = 0.f, r1 = 0.f;
+      // rs: the tile's unrounded row-sum share; rb (bf16): the same over the rounded P
+      auto expo = [&](float moff, float& rs, float& rb) __attribute__((always_inline)) {
+        float r0 = 0.f, r1 = 0.f, b0 = 0.f, b1 = 0.f;
+        if constexpr (FP8) {
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int kb = w >> 2, i = 4 * (w & 3);
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 0], c, moff));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, moff));
-          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 2], c, moff));
-          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 3], c, moff));
-          if (kb == 0) r0 += (p0 + p1) + (p2 + p3);
-          else r1 += (p0 + p1) + (p2 + p3);
-          // the first conversion writes the low half-word only; the word of two
-          // tiles back is passed as the kept half so that nothing is cleared
-          int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[w], false);
-          pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
+          for (int w = 0; w < 8; ++w) {
+            const int kb = w >> 2, i = 4 * (w & 3);
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 0], c, moff));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, moff));
+            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 2], c, moff));
+            const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 3], c, moff));
+            if (kb == 0) r0 += (p0 + p1) + (p2 + p3);
+            else r1 += (p0 + p1) + (p2 + p3);
+            // the first conversion writes the low half-word only; the word of two
+            // tiles back is passed as the kept half so that nothing is cleared
+            int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[w], false);
+            pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 16; ++w) {
+            const int kg = w >> 2, kb = kg >> 1, i = 8 * (kg & 1) + 2 * (w & 3);
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 0], c, moff));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, moff));
+            const unsigned pk = pack_bf16(p0, p1);
+            pw[w] = (int)pk;
+            if (kb == 0) {
+              r0 += p0 + p1;
+              b0 = sum_bf16x2(pk, b0);
+            } else {
+              r1 += p0 + p1;
+              b1 = sum_bf16x2(pk, b1);
+            }
+          }
         }
         rs = r0 + r1;
+        rb = b0 + b1;
       };
-      float moff = kPre - (m == -INFINITY ? 0.f : m);
-      float rs;
-      expo(moff, rs);
+      float rs, rb;
+      expo(moff, rs, rb);
       if constexpr (decltype(sched_c)::value) {
-        // Interleave: the eight MFMAs of mma() one by one, each followed by its
-        // share of the softmax VALU work and the LDS operand reads of the MFMA
-        // two places later.
-#define HAT_SLOT(nds)                                    \
+        // Interleave: the MFMAs of mma() one by one, each followed by its share
+        // of the softmax VALU work and the LDS operand reads of the MFMA two
+        // places later (fp8: 8 MFMAs, 2 or 4 reads each; bf16: 32 MFMAs, 1 or 2).
+#define HAT_SLOT(nds, nv)                                \
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     \
   __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);   \
-  __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        HAT_SLOT(2) HAT_SLOT(4) HAT_SLOT(2) HAT_SLOT(4) HAT_SLOT(2) HAT_SLOT(4) HAT_SLOT(0) HAT_SLOT(0)
+  __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
+        if constexpr (FP8) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          HAT_SLOT(2, 14) HAT_SLOT(4, 14) HAT_SLOT(2, 14) HAT_SLOT(4, 14)
+          HAT_SLOT(2, 14) HAT_SLOT(4, 14) HAT_SLOT(0, 14) HAT_SLOT(0, 14)
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4)
+          HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4)
+          HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4)
+          HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4)
+          HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4)
+          HAT_SLOT(0, 4) HAT_SLOT(0, 4)
+        }
 #undef HAT_SLOT
       }
-      if (__any(m == -INFINITY || !(rs <= 256.f))) {
+      // In steady iterations tile 0 has given every row a finite m, so only
+      // the size check remains; the edges also re-base while m is -inf.
+      const bool need = decltype(sched_c)::value ? !(rs <= 256.f) : (m == -INFINITY || !(rs <= 256.f));
+      if (__any(need)) {
         keep();
         // the scores pass through an empty asm here, so that the row max below
         // cannot be speculated ahead of the branch into the common path
@@ -660,13 +761,16 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
         const float mnew = fmaxf(m, xor32_max(mx) * fabsf(c));
         const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 when m was -inf
         l *= (double)alpha;
+        lf *= alpha;
+        if constexpr (!FP8) dl *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] *= alpha;
         m = mnew;
         moff = kPre - (m == -INFINITY ? 0.f : m);
-        expo(moff, rs);
+        expo(moff, rs, rb);
       }
-      l += (double)rs;
+      lf += rs;
+      if constexpr (!FP8) dl += rb - rs;
     };
 
     // The wave's bounds, made provably wave-uniform so that the loops below
@@ -677,50 +781,55 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
                                                            : Skv / kBN);
     const int ss_end = min(w_nt - 1, w_fm);
     // One iteration with its parts decided at run time (the edges of the loop).
-    auto edge = [&](int u, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], int (&pc)[8], const int (&pp)[8])
+    auto edge = [&](int u, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], int (&pc)[NPW], const int (&pp)[NPW])
         __attribute__((always_inline)) {
-      psync(u);
-      mma(sn, pp, (u + 1) & 3, (u + 3) & 3, u + 1 < w_nt, u >= 1 && u <= w_nt);
+      if (u % kSync == 0) psync(u);
+      mma(sn, pp, (u + 1) % NS, (u + NS - 1) % NS, u + 1 < w_nt, u >= 1 && u <= w_nt);
       __builtin_amdgcn_sched_barrier(0);   // edges are rare: not interleaved, fewer live registers
       auto none = []() __attribute__((always_inline)) {};
       if (u < w_nt) {
         if (u >= w_fm) softmax(sc, pc, std::true_type{}, u, std::false_type{}, none);
         else softmax(sc, pc, std::false_type{}, u, std::false_type{}, none);
+        flush();
       }
     };
     // A steady iteration: every part runs, unmasked, interleaved.
-    auto steady = [&](int u, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], int (&pc)[8], const int (&pp)[8], int kslot,
-                      int vslot) __attribute__((always_inline)) {
-      psync(u);
+    auto steady = [&](int u, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], int (&pc)[NPW], const int (&pp)[NPW], int kslot,
+                      int vslot, auto sync_c) __attribute__((always_inline)) {
+      if constexpr (decltype(sync_c)::value) psync(u);
       mma(sn, pp, kslot, vslot, true, true);
       auto keep = [&]() __attribute__((always_inline)) { asm volatile("" ::"v"(sn[0]), "v"(sn[1])); };
       softmax(sc, pc, std::false_type{}, u, std::true_type{}, keep);
     };
 
-    // Prologue: K(0..3) and V(0..1) in the order of the iterations that
-    // would have queued them; wait for K(0), then S(0).
-    if (ntot > 0) issue_k(0, 0);
-    if (ntot > 1) issue_k(1, 1);
-    if (ntot > 2) issue_k(2, 2);
-    if (ntot > 0) issue_v(0, 0);
-    if (ntot > 3) issue_k(3, 3);
-    if (ntot > 1) issue_v(1, 1);
-    if (ntot >= 4) wait_vmcnt<5 * PWK>();
-    else if (ntot == 3) wait_vmcnt<4 * PWK>();
-    else if (ntot == 2) wait_vmcnt<3 * PWK>();
-    else wait_vmcnt<PWK>();
+    // Prologue: K(0 .. kSync) and V(0 .. kSync-2), then S(0); iteration 0
+    // queues the next ones.
+#pragma unroll
+    for (int x = 0; x <= kSync; ++x)
+      if (x < ntot) issue_k(x, x);
+#pragma unroll
+    for (int x = 0; x <= kSync - 2; ++x)
+      if (x < ntot) issue_v(x, x);
+    wait_vmcnt<0>();
     __syncthreads();
     if (w_nt > 0) mma(S[0], P[1], 0, 0, true, false);
     if (ntot > 0) {
       edge(0, S[0], S[1], P[0], P[1]);
       int u = 1;
-      // Steady iterations four at a time (u = 1 mod 4 at the top), so that the
-      // ring slots and buffers are compile-time constants.
-      for (; u + 3 < ss_end; u += 4) {
-        steady(u + 0, S[1], S[0], P[1], P[0], 2, 0);
-        steady(u + 1, S[0], S[1], P[0], P[1], 3, 1);
-        steady(u + 2, S[1], S[0], P[1], P[0], 0, 2);
-        steady(u + 3, S[0], S[1], P[0], P[1], 1, 3);
+      // Steady iterations eight at a time (u = 1 mod 8 at the top), so that the
+      // ring slots, buffers and barriers are compile-time constants.
+      constexpr std::false_type no{};
+      constexpr std::true_type yes{};
+      for (; u + 7 < ss_end; u += 8) {
+        steady(u + 0, S[1], S[0], P[1], P[0], 2, 0, no);
+        steady(u + 1, S[0], S[1], P[0], P[1], 3, 1, no);
+        steady(u + 2, S[1], S[0], P[1], P[0], 4, 2, no);
+        steady(u + 3, S[0], S[1], P[0], P[1], 5, 3, yes);   // u + 3 = 0 mod 4
+        steady(u + 4, S[1], S[0], P[1], P[0], 6, 4, no);
+        steady(u + 5, S[0], S[1], P[0], P[1], 7, 5, no);
+        steady(u + 6, S[1], S[0], P[1], P[0], 0, 6, no);
+        steady(u + 7, S[0], S[1], P[0], P[1], 1, 7, yes);   // u + 7 = 0 mod 8
+        flush();
       }
       // The rest (u is odd here), two at a time with compile-time buffers.
       for (; u <= ntot; u += 2) {
@@ -1182,3 +1291,4 @@ extern "C" attn_status_t attn_fwd_splitkv(const void* q, const void* k, const vo
   return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, q_descale, k_descale,
                 v_descale, 0, n_splits, workspace, workspace_bytes, stream, -1, -1, 0, tail_only);
 }
+

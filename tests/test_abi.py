@@ -93,6 +93,15 @@ P = 1 << 20
     (dict(Sq=16776960, D=64), 6),            # one past the largest D64 query slice
     (dict(kv_start=(1 << 30) - 100), 6),     # key positions must stay below 2^30
     (dict(kv_start=(1 << 30) - 65, Skv=1), 6),    # kv_start + Skv + one key tile = 2^30
+    # zero sizes: nothing to compute is OK and enqueues nothing, even with null pointers
+    (dict(B=0), 0),
+    (dict(Sq=0), 0),
+    (dict(Hq=0, Hkv=0), 0),
+    (dict(Sq=0, q=None, out=None, lse=None, k=None, v=None), 0),
+    # lse needs 4-byte alignment only: a 4-aligned lse passes the alignment check and is
+    # stopped by the next one (index overflow), a 2-aligned one is not
+    (dict(lse=P + 4, Sq=1 << 30), 6),
+    (dict(lse=P + 2, Sq=1 << 30), 5),
 ])
 def test_fail_closed_validation(L, args, status):
     a = dict(q=P, k=P, v=P, out=P, lse=P, B=1, Hq=4, Hkv=2, Sq=100, Skv=100, D=128, scale=0.1,

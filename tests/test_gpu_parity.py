@@ -245,3 +245,4 @@ def test_attn_fwd_entry_point(fmt, causal):
     torch.cuda.synchronize()
     check_any(inp, O.float().cpu().numpy(), L.cpu().numpy(), refs(inp, scale, causal),
               what=f"attn_fwd {fmt} causal={causal}")
+
