@@ -4,8 +4,8 @@ Argument marshalling only: every step of the attention runs in the HIP
 kernels behind the C ABI declared in ``include/attn.h``. The functions
 ``attn_fwd``, ``attn_fwd_chunk``, ``attn_fwd_window``, ``attn_fwd_splitkv``,
 ``attn_splitkv_workspace_bytes``, ``attn_splitkv_auto_splits``,
-``attn_bwd``, ``attn_bwd_chunk``, ``attn_bwd_workspace_bytes``, ``attn_merge_lse2_host`` and
-``attn_status_string`` carry the C names and
+``attn_bwd``, ``attn_bwd_chunk``, ``attn_bwd_workspace_bytes``, ``attn_fwd_splitkv_static``,
+``attn_merge_lse2_host`` and ``attn_status_string`` carry the C names and
 arguments one for one (pointer arguments accept a torch tensor, a plain integer
 address or None) and return what the C function returns. ``forward`` and
 ``forward_splitkv`` are convenience wrappers that read the sizes off torch
@@ -24,6 +24,7 @@ __all__ = [
     "attn_fwd", "attn_fwd_chunk", "attn_fwd_window", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
     "attn_splitkv_auto_splits", "attn_merge_lse2_host", "attn_status_string", "forward",
     "forward_splitkv", "merge_lse2_host", "attn_bwd", "attn_bwd_chunk", "attn_bwd_workspace_bytes", "backward",
+    "attn_fwd_splitkv_static", "SPLITKV_STATIC_SCRATCH_BYTES",
 ]
 
 ATTN_BF16 = 0
@@ -35,7 +36,8 @@ STATUS = {
 }
 EXPORTED = ("attn_fwd", "attn_fwd_chunk", "attn_fwd_window", "attn_fwd_splitkv", "attn_splitkv_workspace_bytes",
             "attn_splitkv_auto_splits", "attn_merge_lse2_host", "attn_status_string", "attn_bwd",
-            "attn_bwd_chunk", "attn_bwd_workspace_bytes")
+            "attn_bwd_chunk", "attn_bwd_workspace_bytes", "attn_fwd_splitkv_static")
+SPLITKV_STATIC_SCRATCH_BYTES = 64 << 20   # ATTN_SPLITKV_STATIC_SCRATCH_BYTES of attn.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libattn.so")
@@ -65,6 +67,8 @@ def lib():
         L.attn_fwd_window.restype = i32
         L.attn_fwd_splitkv.argtypes = fwd_args + [i64, vp, i64, vp]
         L.attn_fwd_splitkv.restype = i32
+        L.attn_fwd_splitkv_static.argtypes = fwd_args + [i64, vp]
+        L.attn_fwd_splitkv_static.restype = i32
         L.attn_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
         L.attn_splitkv_workspace_bytes.restype = i64
         L.attn_splitkv_auto_splits.argtypes = [i64, i64, i64, i64, i64]
@@ -135,6 +139,15 @@ def attn_fwd_splitkv(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, d
                                   D, float(scale), int(bool(causal)), int(dtype),
                                   _addr(q_descale), _addr(k_descale), _addr(v_descale), int(n_splits),
                                   _addr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def attn_fwd_splitkv_static(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype,
+                            q_descale=None, k_descale=None, v_descale=None, n_splits=0, stream=0):
+    return lib().attn_fwd_splitkv_static(_addr(q), _addr(k), _addr(v), _addr(out), _addr(lse), B, Hq, Hkv, Sq,
+                                         Skv, D, float(scale), int(bool(causal)), int(dtype),
+                                         _addr(q_descale), _addr(k_descale), _addr(v_descale), int(n_splits),
+                                         _stream(stream))
+
 
 
 def attn_splitkv_workspace_bytes(B, Hq, Sq, D, n_splits):

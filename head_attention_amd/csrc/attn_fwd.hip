@@ -58,6 +58,7 @@
 #include <stdint.h>
 #include <type_traits>
 #include <algorithm>
+#include <mutex>
 
 #include "attn.h"
 #include "device_common.h"
@@ -1292,3 +1293,43 @@ extern "C" attn_status_t attn_fwd_splitkv(const void* q, const void* k, const vo
                 v_descale, 0, n_splits, workspace, workspace_bytes, stream, -1, -1, 0, tail_only);
 }
 
+// ---- attn_fwd_splitkv_static: the split partials in a static device array ----
+//
+// For callers that cannot allocate device memory (code under stream capture,
+// tight serving loops, harnesses that forbid allocation): the split-KV
+// forward with its fp32 partials in `scratch`, a file-scope device array of
+// kStaticScratchBytes that every GPU the library runs on holds until the
+// process ends. Host code never uses the array's name as an address (on the
+// host it only names the symbol): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current and kept.
+static constexpr int64_t kStaticScratchBytes = ATTN_SPLITKV_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+extern "C" attn_status_t attn_fwd_splitkv_static(const void* q, const void* k, const void* v, void* out, float* lse,
+                                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                                                 int64_t D, float scale, int causal, attn_dtype_t dtype,
+                                                 const float* q_descale, const float* k_descale,
+                                                 const float* v_descale, int64_t n_splits, void* stream) {
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return ATTN_ERR_HIP;
+  // The partials need not start at any value: every split writes all of its
+  // rows before the merge kernel (same stream) reads them. Launch checks the
+  // split count's need against the array's size (ATTN_ERR_WORKSPACE beyond it).
+  return attn_fwd_splitkv(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, dtype, q_descale, k_descale,
+                          v_descale, n_splits, ws, kStaticScratchBytes, stream);
+}

@@ -46,6 +46,10 @@
 extern "C" {
 #endif
 
+/* Size in bytes of the static device array attn_fwd_splitkv_static keeps its split
+ * partials in (one per GPU). */
+#define ATTN_SPLITKV_STATIC_SCRATCH_BYTES ((int64_t)64 << 20)
+
 typedef enum {
   ATTN_BF16 = 0,        /* q, k, v hold bf16 */
   ATTN_FP8_E4M3FN = 1   /* q, k, v hold e4m3fn codes; real value = decode(code) * descale */
@@ -188,6 +192,26 @@ attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void
                                float scale, int causal, attn_dtype_t dtype,
                                const float* q_descale, const float* k_descale, const float* v_descale,
                                int64_t n_splits, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_splitkv_static — attn_fwd_splitkv without a workspace argument, for
+ * callers that cannot allocate device memory (code under stream/graph
+ * capture, tight serving loops, harnesses that forbid allocation). The split
+ * partials live in a static device array of ATTN_SPLITKV_STATIC_SCRATCH_BYTES
+ * (64 MiB) that each GPU the library runs on holds until the process ends; the
+ * call itself allocates nothing. The caller still passes inputs and outputs.
+ * Arguments and results as attn_fwd_splitkv (n_splits = 0: the library's
+ * choice); ATTN_ERR_WORKSPACE when the chosen split count needs more than the
+ * array holds (attn_splitkv_workspace_bytes > 64 MiB; nothing is launched),
+ * ATTN_ERR_HIP when the array's device address cannot be obtained. Every call
+ * on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (different streams, or different threads) race and must not be issued.
+ */
+attn_status_t attn_fwd_splitkv_static(const void* q, const void* k, const void* v, void* out, float* lse,
+                                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D,
+                                      float scale, int causal, attn_dtype_t dtype,
+                                      const float* q_descale, const float* k_descale, const float* v_descale,
+                                      int64_t n_splits, void* stream);
 
 /* Bytes of workspace attn_fwd_splitkv needs for n_splits (0 when n_splits <= 1;
  * n_splits * B * Hq * Sq * (D + 1) * 4), or -1 on invalid arguments. */
