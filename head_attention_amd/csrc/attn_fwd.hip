@@ -171,7 +171,12 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   int bh, qt;
   if (CAUSAL) {  // longest rows first
     qt = p.n_qtiles - 1 - bid / BH;
-    bh = bid % BH;
+    // Within one query-tile row of the grid, workgroup r goes to XCD r % 8:
+    // when the heads split evenly over the XCDs, give XCD x the contiguous
+    // heads [x BH/8, (x+1) BH/8), which share key/value heads under grouped
+    // heads (and the batch entry).
+    const int r = bid % BH;
+    bh = (BH & 7) == 0 ? (r & 7) * (BH >> 3) + (r >> 3) : r;
   } else {
     bh = bid / p.n_qtiles;
     qt = bid % p.n_qtiles;

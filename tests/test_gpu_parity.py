@@ -246,3 +246,18 @@ def test_attn_fwd_entry_point(fmt, causal):
     check_any(inp, O.float().cpu().numpy(), L.cpu().numpy(), refs(inp, scale, causal),
               what=f"attn_fwd {fmt} causal={causal}")
 
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_negative_k_descale(causal):
+    """fp8 with q_descale * k_descale < 0: the K codes with their sign bits flipped and a
+    negated k_descale hold the same real K, so the oracle is unchanged. The kernel must
+    take the row max from the smallest code product and still give masked keys p = 0."""
+    B, Hq, Hkv, Sq, Skv, D = 1, 2, 1, 300, 333, 128
+    say(f"case negative k_descale causal={causal}")
+    inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, "e4m3fn", seed=41 + causal)
+    neg = dict(inp, k=np.ascontiguousarray(inp["k"] ^ np.uint8(0x80)), k_descale=-inp["k_descale"])
+    import oracle
+    assert np.array_equal(oracle.dequantise(neg["k"], "e4m3fn", neg["k_descale"]),
+                          oracle.dequantise(inp["k"], "e4m3fn", inp["k_descale"]))
+    O, L, _ = run_gpu(neg, 1 / math.sqrt(D), causal)
+    check_any(neg, O, L, refs(inp, 1 / math.sqrt(D), causal), what=f"negative k_descale causal={causal}")
