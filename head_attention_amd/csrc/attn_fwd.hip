@@ -609,8 +609,18 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       const i32x4 k1 = *(const LDS_AS i32x4*)(kp + koff[2 * dc + 1]);
       return i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
     };
+    // The V ring starts at 64 KB, beyond the 16-bit offset field of an LDS
+    // read: its base goes into the address registers once (opaque to the
+    // compiler, which would otherwise OR ring, slot and key-group constants
+    // into a fresh register for every read), leaving offsets below 64 KB.
+    int vbase[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      vbase[db] = VRING + voff[db];
+      asm volatile("" : "+v"(vbase[db]));
+    }
     auto vload8 = [&](int slot, int db) __attribute__((always_inline)) {
-      const LDS_AS char* vp = smem + VRING + slot * T::BYTES + voff[db];
+      const LDS_AS char* vp = smem + vbase[db] + slot * T::BYTES;
       int vw[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -683,6 +693,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       auto expo = [&](float moff, float& rs, float& rb) __attribute__((always_inline)) {
         float r0 = 0.f, r1 = 0.f, b0 = 0.f, b1 = 0.f;
         if constexpr (FP8) {
+          float gs[8];   // sums of four; a tree from these needs no zero start
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
             const int kb = w >> 2, i = 4 * (w & 3);
@@ -690,8 +701,9 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, moff));
             const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 2], c, moff));
             const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 3], c, moff));
-            if (kb == 0) r0 += (p0 + p1) + (p2 + p3);
-            else r1 += (p0 + p1) + (p2 + p3);
+            gs[w] = (p0 + p1) + (p2 + p3);
+            if (w == 3) r0 = (gs[0] + gs[1]) + (gs[2] + gs[3]);
+            if (w == 7) r1 = (gs[4] + gs[5]) + (gs[6] + gs[7]);
             // the first conversion writes the low half-word only; the word of two
             // tiles back is passed as the kept half so that nothing is cleared
             int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[w], false);
