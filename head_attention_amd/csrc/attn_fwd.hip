@@ -259,8 +259,9 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   // memory-counter waits for Q then never wait for the copies.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-  // Clear the ring once, so that tail rows never expose uninitialised LDS.
-  for (int i = threadIdx.x; i < kStages * 2 * T::BYTES / 16; i += kThr)
+  // Clear all of LDS once (both rings), so that tail rows never expose
+  // uninitialised LDS.
+  for (int i = threadIdx.x; i < kLds / 16; i += kThr)
     *(LDS_AS u32x4*)(smem + i * 16) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
@@ -389,23 +390,33 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
 
     // ---- online softmax (base 2) with a checked running max. p = exp2(c s - m)
     // is formed with the current m; while every p of the tile stays at most
-    // 2^8 (a lane's partial row sum bounds its p) m is good enough and no row
-    // max is needed. Otherwise (or while m is still -inf) m becomes the exact
-    // running max, O and l are rescaled, and p is formed again.
+    // 2^8 m is good enough and no row max is needed. The check is on the
+    // lane's partial sums over each 32-key block (16 p each, bounding every
+    // one of them): while no score exceeds m every p is at most 2^kPre and
+    // those sums at most 2^8, so only a tile that raises the max can fail it.
+    // Otherwise (or while m is still -inf) the tile's row max is taken and, if
+    // it exceeds m in any row, m becomes the exact running max, O and l are
+    // rescaled, and p is formed again.
     f32x16 sraw[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sraw[kb] = s[kb];
     float moff = kPre - (m == -INFINITY ? 0.f : m);
-    float rs = 0.f;
+    float rk[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, moff));
         s[kb][i] = pv;
-        rs += pv;
+        rk[kb] = i == 0 ? pv : rk[kb] + pv;
       }
-    if (__any(m == -INFINITY || !(rs <= 256.f))) {
+    float rs = rk[0], rx = rk[0];
+#pragma unroll
+    for (int kb = 1; kb < NKB; ++kb) {
+      rs += rk[kb];
+      rx = fmaxf(rx, rk[kb]);
+    }
+    if (__any(m == -INFINITY || !(rx <= 256.f))) {
       float mx = -INFINITY;   // max of s, or of -s when c < 0
       if (!cneg) {
 #pragma unroll
@@ -419,22 +430,26 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, -sraw[kb][i]);
       }
       const float mnew = fmaxf(m, xor32_max(mx) * fabsf(c));
-      const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 when m was -inf
-      l *= (double)alpha;
-      if constexpr (!FP8) dl *= alpha;
+      // If no row's max grew (say every row is still fully masked), the pass
+      // above stands.
+      if (__any(mnew > m)) {
+        const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 when m was -inf
+        l *= (double)alpha;
+        if constexpr (!FP8) dl *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      m = mnew;
-      moff = kPre - (m == -INFINITY ? 0.f : m);
-      rs = 0.f;
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        m = mnew;
+        moff = kPre - (m == -INFINITY ? 0.f : m);
+        rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sraw[kb][i], c, moff));
-          s[kb][i] = pv;
-          rs += pv;
-        }
+          for (int i = 0; i < 16; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sraw[kb][i], c, moff));
+            s[kb][i] = pv;
+            rs += pv;
+          }
+      }
     }
     l += (double)rs;
 
@@ -689,8 +704,9 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
             sc[kb][i] = ok ? sc[kb][i] : smask;
           }
       }
-      // rs: the tile's unrounded row-sum share; rb (bf16): the same over the rounded P
-      auto expo = [&](float moff, float& rs, float& rb) __attribute__((always_inline)) {
+      // rs: the tile's unrounded row-sum share; rx: the larger of its two 32-key
+      // block shares (the size check); rb (bf16): rs over the rounded P
+      auto expo = [&](float moff, float& rs, float& rx, float& rb) __attribute__((always_inline)) {
         float r0 = 0.f, r1 = 0.f, b0 = 0.f, b1 = 0.f;
         if constexpr (FP8) {
           float gs[8];   // sums of four; a tree from these needs no zero start
@@ -727,10 +743,11 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
           }
         }
         rs = r0 + r1;
+        rx = fmaxf(r0, r1);
         rb = b0 + b1;
       };
-      float rs, rb;
-      expo(moff, rs, rb);
+      float rs, rx, rb;
+      expo(moff, rs, rx, rb);
       if constexpr (decltype(sched_c)::value) {
         // Interleave: the MFMAs of mma() one by one, each followed by its share
         // of the softmax VALU work and the LDS operand reads of the MFMA two
@@ -758,7 +775,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       }
       // In steady iterations tile 0 has given every row a finite m, so only
       // the size check remains; the edges also re-base while m is -inf.
-      const bool need = decltype(sched_c)::value ? !(rs <= 256.f) : (m == -INFINITY || !(rs <= 256.f));
+      const bool need = decltype(sched_c)::value ? !(rx <= 256.f) : (m == -INFINITY || !(rx <= 256.f));
       if (__any(need)) {
         keep();
         // the scores pass through an empty asm here, so that the row max below
@@ -777,15 +794,18 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, -sc[kb][i]);
         }
         const float mnew = fmaxf(m, xor32_max(mx) * fabsf(c));
-        const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 when m was -inf
-        l *= (double)alpha;
-        lf *= alpha;
-        if constexpr (!FP8) dl *= alpha;
+        // no row's max grew (say every row still fully masked): the pack stands
+        if (__any(mnew > m)) {
+          const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 when m was -inf
+          l *= (double)alpha;
+          lf *= alpha;
+          if constexpr (!FP8) dl *= alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-        m = mnew;
-        moff = kPre - (m == -INFINITY ? 0.f : m);
-        expo(moff, rs, rb);
+          for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+          m = mnew;
+          moff = kPre - (m == -INFINITY ? 0.f : m);
+          expo(moff, rs, rx, rb);
+        }
       }
       lf += rs;
       if constexpr (!FP8) dl += rb - rs;

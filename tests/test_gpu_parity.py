@@ -20,6 +20,7 @@ import torch
 import head_attention_amd as ha
 from gpu_helpers import (say, run_gpu, oracle_ref, oracle_full, refs, check_any, synth_inputs, check_bf16,
                          check_fp8, make_inputs, WORKLOADS, nrms, frob_rel, to_dev, descale_dev)
+from synth import normal, to_bf16_bits, quant_e4m3fn_per_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -261,3 +262,35 @@ def test_negative_k_descale(causal):
                           oracle.dequantise(inp["k"], "e4m3fn", inp["k_descale"]))
     O, L, _ = run_gpu(neg, 1 / math.sqrt(D), causal)
     check_any(neg, O, L, refs(inp, 1 / math.sqrt(D), causal), what=f"negative k_descale causal={causal}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3fn"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_flat_scores_then_a_peak(fmt, D, causal):
+    """Near-uniform scores (keys scaled by 0.01) over 47 key tiles, with two keys of
+    norm about 4 sqrt(D) late in the sequence. On the flat tiles the fp8 p all sit near
+    2^4, their lane sums pass the 2^8 check, and the row max is found unchanged (m is
+    kept); the two strong keys then raise the max of about half the rows, which must
+    rescale O and l. Both the kept-m and the re-base path meet the usual bars."""
+    B, Hq, Hkv, Sq, Skv = 1, 2, 1, 300, 3000
+    say(f"case flat scores then a peak fmt={fmt} D={D} causal={causal}")
+    inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, fmt, seed=61 + D + causal, scale_k=0.01)
+    k32 = inp["k32"].clone()
+    for j in (1500, 2900):
+        k32[:, :, j] = normal((B, Hkv, D), 1000 + j) * 4.0
+    inp = _with_k(inp, k32)
+    scale = 1 / math.sqrt(D)
+    O, L, _ = run_gpu(inp, scale, causal)
+    check_any(inp, O, L, refs(inp, scale, causal), what=f"flat then peak {fmt} D={D} causal={causal}")
+
+
+def _with_k(inp, k32):
+    """The stored inputs with K replaced (re-encoded in the inputs' format)."""
+    out = dict(inp, k32=k32)
+    if inp["fmt"] == "bf16":
+        out["k"] = to_bf16_bits(k32)
+    else:
+        kc, kd = quant_e4m3fn_per_tensor(k32)
+        out.update(k=kc, k_descale=float(kd))
+    return out
