@@ -16,8 +16,10 @@ section) exactly, which tests/test_oracle_pins.py checks.
 
 After the timed steps (outside them) the line also carries ``mfma_ceiling``:
 what an MFMA-only loop with random operands sustains on the device
-(libmfma_probe.so), and each dtype's fraction of it, beside the fraction of
-the published dense peak that ``roofline`` reports.
+(libmfma_probe.so), and the same MFMAs with the attention tile's own softmax
+VALU instructions interleaved (``with_softmax``), and each dtype's fraction of
+both, beside the fraction of the published dense peak that ``roofline``
+reports.
 """
 
 import argparse
@@ -408,8 +410,11 @@ def mfma_ceiling(dev):
     """What the matrix cores sustain on this device with nothing else running: the
     MFMA-only loop of libmfma_probe.so (the attention kernels' bf16 32x32x16 and fp8
     32x32x64 forms, random register operands rotated per MFMA, two waves per SIMD), timed
-    with HIP events over launches of ~15 ms, after the attention timing. Also the dense
-    peak from the device's CU count and peak clock. None when the probe is not built."""
+    with HIP events over launches of ~15 ms, after the attention timing; and under
+    ``with_softmax`` the same MFMAs each followed by its share of the attention tile's
+    softmax VALU instructions (the best an attention loop with that instruction mix can
+    do here). Also the dense peak from the device's CU count and peak clock. None when
+    the probe is not built."""
     import ctypes
     import numpy as np
     import torch
@@ -420,6 +425,8 @@ def mfma_ceiling(dev):
     L.mfma_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p]
     L.mfma_probe_launch.restype = ctypes.c_int
+    L.mfma_softmax_probe_launch.argtypes = L.mfma_probe_launch.argtypes
+    L.mfma_softmax_probe_launch.restype = ctypes.c_int
     L.mfma_probe_device.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     L.mfma_probe_device.restype = ctypes.c_int
     cus, clk = ctypes.c_int(0), ctypes.c_int(0)
@@ -434,10 +441,18 @@ def mfma_ceiling(dev):
     stream = torch.cuda.current_stream()
     res = {"kernel": "MFMA-only loop (libmfma_probe.so): random register operands rotated per MFMA, "
                      "4 independent accumulators, 2 waves per SIMD", "unit": "TFLOP/s"}
-    for name, fp8, src, iters, fl in (("bf16", 0, src_b, 50000, 32768), ("fp8", 1, src_8, 25000, 131072)):
+    res["with_softmax"] = {
+        "kernel": "the same MFMAs, each followed by its share of the attention tile's softmax VALU work "
+                  "(fp8: 4 fma, 4 exp2, 4 add, 2 e4m3fn packs per MFMA; bf16: 1 fma, 1 exp2, 1 add and every "
+                  "other MFMA a bf16 pack and a dot2), interleaved in each wave", "unit": "TFLOP/s"}
+    runs = [(res, L.mfma_probe_launch, "bf16", 0, src_b, 50000, 32768),
+            (res, L.mfma_probe_launch, "fp8", 1, src_8, 25000, 131072),
+            (res["with_softmax"], L.mfma_softmax_probe_launch, "bf16", 0, src_b, 40000, 32768),
+            (res["with_softmax"], L.mfma_softmax_probe_launch, "fp8", 1, src_8, 15000, 131072)]
+    for into, fn, name, fp8, src, iters, fl in runs:
         def call():
-            if L.mfma_probe_launch(fp8, nblocks, iters, src.data_ptr(), out.data_ptr(), stream.cuda_stream) != 0:
-                raise RuntimeError("mfma_probe_launch failed")
+            if fn(fp8, nblocks, iters, src.data_ptr(), out.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError("MFMA probe launch failed")
         for _ in range(3):
             call()
         torch.cuda.synchronize()
@@ -449,7 +464,7 @@ def mfma_ceiling(dev):
             e1.record(stream)
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e-3)
-        res[name] = round(nblocks * 4 * iters * 8 * fl / float(np.median(ts)) / 1e12, 1)
+        into[name] = round(nblocks * 4 * iters * 8 * fl / float(np.median(ts)) / 1e12, 1)
     mhz = clk.value / 1e3
     res["device"] = {"cus": cus.value, "peak_clock_mhz": mhz,
                      "dense_peak_bf16": round(cus.value * mhz * 1e6 * 4096 / 1e12, 1),
@@ -778,9 +793,14 @@ def main():
         if ceil:
             out["per_dtype"]["bf16"]["frac_of_measured_ceiling"] = round(tf_b / ceil["bf16"], 4)
             out["per_dtype"]["fp8"]["frac_of_measured_ceiling"] = round(tf_8 / ceil["fp8"], 4)
+            mix = ceil["with_softmax"]
+            out["per_dtype"]["bf16"]["frac_of_mfma_softmax_ceiling"] = round(tf_b / mix["bf16"], 4)
+            out["per_dtype"]["fp8"]["frac_of_mfma_softmax_ceiling"] = round(tf_8 / mix["fp8"], 4)
             print(f"# MFMA-only ceiling: bf16 {ceil['bf16']} TFLOP/s, fp8 {ceil['fp8']} TFLOP/s; device dense peak "
                   f"{ceil['device']['dense_peak_bf16']} / {ceil['device']['dense_peak_fp8']} TFLOP/s "
-                  f"({ceil['device']['cus']} CUs at {ceil['device']['peak_clock_mhz']} MHz)", file=sys.stderr, flush=True)
+                  f"({ceil['device']['cus']} CUs at {ceil['device']['peak_clock_mhz']} MHz); with the softmax VALU "
+                  f"mix: bf16 {ceil['with_softmax']['bf16']}, fp8 {ceil['with_softmax']['fp8']} TFLOP/s",
+                  file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(inp_b, wb, args.cpu_seconds)
         out["cpu_baseline"] = cb

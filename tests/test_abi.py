@@ -38,8 +38,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_mfma_probe_library_loads_and_refuses_bad_arguments():
-    """The benchmark's MFMA-only probe (a measurement aid beside the attention library)
-    exports its two entry points and rejects bad arguments without launching."""
+    """The benchmark's MFMA probes (a measurement aid beside the attention library)
+    export their three entry points and reject bad arguments without launching."""
     import ctypes
     path = os.path.join(ROOT, "head_attention_amd", "libmfma_probe.so")
     if not os.path.exists(path):
@@ -53,6 +53,11 @@ def test_mfma_probe_library_loads_and_refuses_bad_arguments():
     assert P.mfma_probe_launch(0, 0, 10, 1 << 20, 1 << 20, None) == 1      # no workgroups
     assert P.mfma_probe_launch(0, 4, 0, 1 << 20, 1 << 20, None) == 1       # no iterations
     assert P.mfma_probe_launch(1, 4, 10, None, 1 << 20, None) == 1         # no operand buffer
+    P.mfma_softmax_probe_launch.argtypes = P.mfma_probe_launch.argtypes
+    P.mfma_softmax_probe_launch.restype = ctypes.c_int
+    assert P.mfma_softmax_probe_launch(1, 0, 10, 1 << 20, 1 << 20, None) == 1
+    assert P.mfma_softmax_probe_launch(0, 4, 0, 1 << 20, 1 << 20, None) == 1
+    assert P.mfma_softmax_probe_launch(1, 4, 10, 1 << 20, None, None) == 1   # no output buffer
 
 
 def test_status_strings(L):
