@@ -12,8 +12,10 @@
 // Design (gfx950 first; nothing here is translated from another kernel):
 //  * One workgroup = 8 wavefronts = 256 query rows of one (batch, head); each
 //    wave owns 32 rows. The grid covers B * Hq * ceil(Sq / 256) workgroups.
-//    A grid small enough to leave half the CUs idle uses workgroups of 4
-//    wavefronts (128 rows) instead, twice as many of them.
+//    A grid small enough to leave half the CUs idle uses workgroups of 128
+//    rows instead, twice as many of them: for bf16 without a window 8
+//    wavefronts in which two share each 32 rows and take alternate key tiles
+//    (merged through LDS at the end), otherwise 4 wavefronts.
 //  * K and V stream through LDS in tiles of 64 keys, in a ring of kStages
 //    slots filled kStages-1 tiles ahead by buffer_load ... lds (global -> LDS
 //    without VGPRs); one workgroup barrier per tile publishes a tile and
@@ -124,11 +126,17 @@ struct Tile {
   }
 };
 
-template <int D, bool CAUSAL, bool FP8, bool WIN, int NW>
+template <int D, bool CAUSAL, bool FP8, bool WIN, int NW, bool KS>
 __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   constexpr int kW = NW;            // waves per workgroup (8, or 4 for grids that leave CUs idle)
   constexpr int kThr = 64 * NW;
-  constexpr int kRows = 32 * NW;    // query rows per workgroup
+  // KS (key split, bf16 without a window): waves w and w + NW/2 own the same
+  // 32 rows and take alternate key tiles, two tiles per barrier step; their
+  // (m, l, O) are merged through LDS at the end. A workgroup then covers
+  // 32 NW/2 rows at two waves per SIMD, for grids too small to fill the CUs.
+  static_assert(!KS || (!FP8 && !WIN && NW == 8), "the key split is a bf16 8-wave mode");
+  constexpr int kRG = KS ? NW / 2 : NW;   // waves with distinct query rows
+  constexpr int kRows = 32 * kRG;         // query rows per workgroup
   using T = Tile<D, FP8>;
   constexpr int ROWB = T::ROWB;
   constexpr int NDB = D / 32;                       // 32-wide output column blocks
@@ -187,8 +195,10 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   const int kv_start = p.kv_start + s0;
   const int b = bh / p.Hq, h = bh % p.Hq, hk = h / p.group;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rw = KS ? wave % kRG : wave;   // the wave's 32-row group
+  [[maybe_unused]] const int kh = KS ? wave / kRG : 0;   // KS: its key half (tiles kh, kh + 2, ...)
   const int g = lane >> 5, n = lane & 31;
-  const int q0 = qt * kRows, qw = q0 + wave * 32, qi = qw + n;
+  const int q0 = qt * kRows, qw = q0 + rw * 32, qi = qw + n;
 
   const size_t qrow0 = (size_t)(b * p.Hq + h) * (size_t)p.Sq;
   const size_t krow0 = (size_t)(b * p.Hkv + hk) * (size_t)p.Skv + (size_t)(Skv > 0 ? s0 : 0);
@@ -319,7 +329,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   // own copies of tile t (the copies of later tiles may still be in flight),
   // then the barrier publishes tile t and retires slot (t-1) % kStages, which
   // is refilled with tile t + kStages - 1.
-  if constexpr (!PIPE) {
+  if constexpr (!PIPE && !KS) {
 #pragma unroll
     for (int u = 0; u < kStages - 1; ++u)
       if (u < ntot) issue(u);
@@ -876,6 +886,64 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
         edge(u + 1, S[0], S[1], P[0], P[1]);
       }
     }
+  } else if constexpr (KS) {
+    // Tiles 2v and 2v+1 (slots 2v % kStages and (2v+1) % kStages) at step v,
+    // by the waves of key half 0 and 1; step v's barrier retires the slots of
+    // step v-1, which take tiles 2v+2 and 2v+3. Every wave runs ceil(ntot/2)
+    // steps (ntot is the workgroup's), so the barriers pair up.
+    const int first_masked = CAUSAL ? min(Skv / kBN, max(0, qw - kv_start + 1) / kBN) : Skv / kBN;
+    const int n_plain = min(first_masked, ntot);
+    if (ntot > 0) issue(0);
+    if (ntot > 1) issue(1);
+    auto ksync = [&](int v) __attribute__((always_inline)) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (2 * v + 2 < ntot) issue(2 * v + 2);
+      if (2 * v + 3 < ntot) issue(2 * v + 3);
+    };
+    int v = 0;
+    for (; 2 * v + 1 < n_plain; ++v) {   // both tiles of the step unmasked for this wave's rows
+      ksync(v);
+      if (2 * v + kh < w_ntiles) step(2 * v + kh, std::false_type{}, kAnySlot);
+    }
+    for (; 2 * v < ntot; ++v) {
+      ksync(v);
+      const int u = 2 * v + kh;
+      if (u < ntot && u < w_ntiles) step(u, std::true_type{}, kAnySlot);
+    }
+    // Merge: key half 1 hands its m, l, dl and O (lane by lane: the same rows
+    // and columns) to key half 0 through LDS; half 0 then writes the output.
+    wait_vmcnt<0>();
+    __syncthreads();   // every ring read done
+    constexpr int NF = NDB * 16 + 4;   // floats per lane: O, m, dl, l (two words)
+    static_assert(kRG * NF * 64 * 4 <= kLds, "merge buffer fits the ring");
+    LDS_AS float* xb = (LDS_AS float*)smem + rw * NF * 64 + lane;
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xb[(db * 16 + i) * 64] = o[db][i];
+      const u32x2 lw = __builtin_bit_cast(u32x2, l);
+      xb[(NF - 4) * 64] = m;
+      xb[(NF - 3) * 64] = dl;
+      xb[(NF - 2) * 64] = __uint_as_float(lw[0]);
+      xb[(NF - 1) * 64] = __uint_as_float(lw[1]);
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = xb[(NF - 4) * 64], dl1 = xb[(NF - 3) * 64];
+    const double l1 = __builtin_bit_cast(double, u32x2{__float_as_uint(xb[(NF - 2) * 64]),
+                                                       __float_as_uint(xb[(NF - 1) * 64])});
+    const float mm = fmaxf(m, m1);
+    const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = o[db][i] * a0 + xb[(db * 16 + i) * 64] * a1;
+    l = l * (double)a0 + l1 * (double)a1;
+    dl = dl * a0 + dl1 * a1;
+    m = mm;
   } else if constexpr (!WIN) {
     const int first_masked = CAUSAL ? min(Skv / kBN, max(0, qw - kv_start + 1) / kBN) : Skv / kBN;
     const int n_plain = min(first_masked, ntot);
@@ -1061,12 +1129,16 @@ typedef void (*kernel_fn)(Params);
 
 template <int D, bool FP8, int NW>
 kernel_fn pick_nw(bool causal, bool win) {
-  if (win) return causal ? attn_fwd_kernel<D, true, FP8, true, NW> : attn_fwd_kernel<D, false, FP8, true, NW>;
-  return causal ? attn_fwd_kernel<D, true, FP8, false, NW> : attn_fwd_kernel<D, false, FP8, false, NW>;
+  if (win)
+    return causal ? attn_fwd_kernel<D, true, FP8, true, NW, false> : attn_fwd_kernel<D, false, FP8, true, NW, false>;
+  return causal ? attn_fwd_kernel<D, true, FP8, false, NW, false> : attn_fwd_kernel<D, false, FP8, false, NW, false>;
 }
 
+// ks: the bf16 key-split instance (8 waves, 128 rows); nw otherwise.
 template <int D, bool FP8>
-kernel_fn pick(bool causal, bool win, int nw) {
+kernel_fn pick(bool causal, bool win, int nw, bool ks) {
+  if constexpr (!FP8)
+    if (ks) return causal ? attn_fwd_kernel<D, true, false, false, 8, true> : attn_fwd_kernel<D, false, false, false, 8, true>;
   return nw == 4 ? pick_nw<D, FP8, 4>(causal, win) : pick_nw<D, FP8, 8>(causal, win);
 }
 
@@ -1132,6 +1204,9 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   // grid of 256-row tiles fills at most half the CUs, so that the doubled grid
   // of half-size workgroups still runs in one round.
   const int nw = nsp == 1 && 2 * B * Hq * ((Sq + kBM - 1) / kBM) <= (int64_t)device_cus() ? 4 : 8;
+  // bf16 without a window runs those 128-row tiles as 8-wave key-split
+  // workgroups instead (two waves per row group, alternate key tiles).
+  const bool ks = nw == 4 && dtype == ATTN_BF16 && !win;
   const int64_t n_qtiles = (Sq + 32 * nw - 1) / (32 * nw);
   const int64_t rows = B * Hq * Sq;
   const int64_t ntiles = B * Hq * n_qtiles;
@@ -1183,9 +1258,9 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   p.sink = (int)std::min(sink, kUnbounded);
 
   kernel_fn fn;
-  if (dtype == ATTN_BF16) fn = D == 128 ? pick<128, false>(causal, win, nw) : pick<64, false>(causal, win, nw);
-  else fn = D == 128 ? pick<128, true>(causal, win, nw) : pick<64, true>(causal, win, nw);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * nw), 0, (hipStream_t)stream, p);
+  if (dtype == ATTN_BF16) fn = D == 128 ? pick<128, false>(causal, win, nw, ks) : pick<64, false>(causal, win, nw, ks);
+  else fn = D == 128 ? pick<128, true>(causal, win, nw, false) : pick<64, true>(causal, win, nw, false);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(ks ? 512 : 64 * nw), 0, (hipStream_t)stream, p);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   if (nsp > 1) {
     const unsigned mgrid = (unsigned)((part_rows + 15) / 16);

@@ -294,3 +294,18 @@ def _with_k(inp, k32):
         kc, kd = quant_e4m3fn_per_tensor(k32)
         out.update(k=kc, k_descale=float(kd))
     return out
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_split_workgroups(D, causal):
+    """A bf16 grid that fills at most half the CUs runs as 8-wave workgroups of 128
+    rows in which two waves share each 32 rows and take alternate key tiles, merged
+    at the end. Shapes with an odd and an even number of key tiles, a ragged key
+    tail, grouped heads and rows past Sq in the last tile; against the oracle."""
+    for (B, Hq, Hkv, Sq, Skv) in ((1, 4, 2, 700, 1050), (2, 2, 1, 300, 1280)):
+        say(f"case key split D={D} causal={causal} B{B} H{Hq}/{Hkv} {Sq}x{Skv}")
+        inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, "bf16", seed=71 + D + causal + Sq)
+        scale = 1 / math.sqrt(D)
+        O, L, _ = run_gpu(inp, scale, causal)
+        check_any(inp, O, L, refs(inp, scale, causal), what=f"key split D={D} causal={causal} {Sq}x{Skv}")
