@@ -297,7 +297,9 @@ def bench_workload(args, w, make_inputs):
         "ms_p95": round(float(np.percentile(tl, 95)) * 1e3, 4), "ms_min": round(float(tl.min()) * 1e3, 4),
         "ms_loop100": round(t_loop * 1e3, 4), "tflops_loop100": round(flops / t_loop / 1e12, 2),
         "frac_of_peak": round(tf / PEAK_TFLOPS[dtn], 4), "key_splits": nsplit if nsplit is not None else 1,
-        "workgroups": w.B * w.Hq * ((w.Sq + 255) // 256),
+        # the library's grid for an unsplit call: 256-row workgroups, or 128-row ones
+        # (twice as many) when the 256-row grid would fill at most half the CUs
+        **grid_of(w, nsplit),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS[dtn], "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_TFLOPS[dtn], 4), "traffic": None,
                      "kernel": f"attn_fwd_kernel<{w.D},{str(causal).lower()},{str(dtn == 'fp8').lower()},"
@@ -404,6 +406,19 @@ SWEEP_SPLIT = [  # B, H, Sq, Skv, D, dtype: few query tiles against long key ran
     (1, 32, 1, 131072, 128, "bf16"), (1, 8, 256, 262144, 128, "bf16"), (1, 1, 256, 1048576, 128, "bf16"),
     (4, 8, 128, 65536, 128, "fp8"), (1, 2, 4096, 524288, 64, "bf16"),
 ]
+
+
+def grid_of(w, nsplit):
+    """Workgroups and rows per workgroup of an unsplit call (None for split calls,
+    whose grid the library sizes from the key splits)."""
+    import torch
+    if nsplit not in (None, 1):
+        return {"workgroups": None, "rows_per_workgroup": None}
+    tiles = w.B * w.Hq * ((w.Sq + 255) // 256)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if 2 * tiles <= cus:
+        return {"workgroups": w.B * w.Hq * ((w.Sq + 127) // 128), "rows_per_workgroup": 128}
+    return {"workgroups": tiles, "rows_per_workgroup": 256}
 
 
 def mfma_ceiling(dev):

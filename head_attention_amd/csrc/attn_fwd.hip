@@ -269,10 +269,13 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   // memory-counter waits for Q then never wait for the copies.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-  // Clear all of LDS once (both rings), so that tail rows never expose
-  // uninitialised LDS.
-  for (int i = threadIdx.x; i < kLds / 16; i += kThr)
-    *(LDS_AS u32x4*)(smem + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  // Clear all of LDS once (both rings), so that the rows of a ragged last
+  // key tile never expose uninitialised LDS. With whole tiles only, every
+  // byte the loop reads is written by a tile copy first, and the clear is
+  // skipped (the condition is the workgroup's own).
+  if (Skv % kBN != 0)
+    for (int i = threadIdx.x; i < kLds / 16; i += kThr)
+      *(LDS_AS u32x4*)(smem + i * 16) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
   // Global -> LDS for tile t into slot t % kStages: the 2*NINSTR 1-KB pieces
