@@ -303,7 +303,7 @@ def bench_workload(args, w, make_inputs):
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS[dtn], "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_TFLOPS[dtn], 4), "traffic": None,
                      "kernel": f"attn_fwd_kernel<{w.D},{str(causal).lower()},{str(dtn == 'fp8').lower()},"
-                               f"{str(local).lower()},*>" + (" + merge_splits_kernel" if nsplit is not None else ""),
+                               f"{str(local).lower()},*,*>" + (" + merge_splits_kernel" if nsplit is not None else ""),
                      "mean_launch_ms": round(float(tl.mean()) * 1e3, 4)},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_workload(inp, w, causal, args.cpu_seconds)}),
         flush=True)
@@ -761,7 +761,7 @@ def main():
         tf = flops / t / 1e12
         return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
                 "frac": round(tf / PEAK_TFLOPS[dt], 4), "traffic": traffic.get(dt),
-                "kernel": f"attn_fwd_kernel<128,false,{'true' if dt == 'fp8' else 'false'},false,8>",
+                "kernel": f"attn_fwd_kernel<128,false,{'true' if dt == 'fp8' else 'false'},false,8,false>",
                 "mean_launch_ms": round(t * 1e3, 4),
                 "algorithmic_bytes": algorithmic_bytes(B, H, H, S, S, D, elt)}
 
