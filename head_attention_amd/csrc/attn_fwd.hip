@@ -584,34 +584,23 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
         if (u + kSync - 1 + j < ntot) issue_v(u + kSync - 1 + j, (u + kSync - 1 + j) % NS);
     };
 
+    static_assert(FP8, "the pipelined loop is the fp8 loop");
     // Per-lane LDS operand offsets (rows 32 apart, and keys 16 apart, share
-    // the swizzle, so tiles and key groups add immediate offsets).
-    //  fp8:  K row n, 16-byte chunk 4 dc + 2 g + h; V (transposing reads) key
-    //        kv0 + 16 i for i = 0..3, chunk 2 db + dgrp.
-    //  bf16: K row n, chunk 2 dc + g; V keys kv0 + 16 kg and + 8, column
-    //        32 db + 16 dgrp + 4 ss.
-    constexpr int NKO = FP8 ? 2 * (D / 64) : D / 16;
+    // the swizzle, so tiles and key groups add immediate offsets): K row n,
+    // 16-byte chunk 4 dc + 2 g + h; V (transposing reads) key kv0 + 16 i for
+    // i = 0..3, chunk 2 db + dgrp.
+    constexpr int NKO = 2 * (D / 64);
     int koff[NKO];
     int voff[NDB];
-    if constexpr (FP8) {
 #pragma unroll
-      for (int dc = 0; dc < D / 64; ++dc)
+    for (int dc = 0; dc < D / 64; ++dc)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) koff[2 * dc + h] = krow * ROWB + (((4 * dc + 2 * g + h) ^ T::kswz(krow)) * 16);
+      for (int h = 0; h < 2; ++h) koff[2 * dc + h] = krow * ROWB + (((4 * dc + 2 * g + h) ^ T::kswz(krow)) * 16);
+    {
       const int rr = l16 >> 1, hh = l16 & 1;
       const int kv0 = 8 * (rr >> 2) + 4 * g + (rr & 3);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) voff[db] = kv0 * ROWB + (((2 * db + dgrp) ^ T::vswz(kv0)) * 16) + 8 * hh;
-    } else {
-#pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) koff[dc] = krow * ROWB + (((2 * dc + g) ^ T::kswz(krow)) * 16);
-      const int rr = l16 >> 2, ss = l16 & 3;
-      const int kv0 = 4 * g + rr;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int col = 32 * db + 16 * dgrp + 4 * ss;
-        voff[db] = kv0 * ROWB + (((col >> 3) ^ T::vswz(kv0)) * 16) + (col & 7) * 2;
-      }
     }
 
     // moff = kPre - m (kPre while m is -inf), changed only by a re-base; lf
@@ -623,7 +612,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       l += (double)lf;
       lf = 0.f;
     };
-    constexpr int NPW = FP8 ? 8 : 16;   // P words per lane and tile (e4m3fn x4 or bf16 x2)
+    constexpr int NPW = 8;   // P words per lane and tile (e4m3fn x4)
     f32x16 S[2][NKB];
     int P[2][NPW];
 #pragma unroll
@@ -658,15 +647,6 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       }
       return i32x8{vw[0], vw[1], vw[2], vw[3], vw[4], vw[5], vw[6], vw[7]};
     };
-    auto kload16 = [&](int slot, int kb, int dc) __attribute__((always_inline)) {
-      return *(const LDS_AS bf16x8*)(smem + KRING + slot * T::BYTES + kb * 32 * ROWB + koff[dc]);
-    };
-    auto vload16 = [&](int slot, int kg, int db) __attribute__((always_inline)) {
-      const LDS_AS char* vp = smem + VRING + slot * T::BYTES + voff[db] + 16 * kg * ROWB;
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)vp);
-      const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + 8 * ROWB));
-      return __builtin_bit_cast(bf16x8, i16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]});
-    };
     auto mfma8 = [](i32x8 a, i32x8 b, f32x16 c) __attribute__((always_inline)) {
       return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
     };
@@ -676,31 +656,17 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
         __attribute__((always_inline)) {
       static_assert(NKB == 2 && NDB == 4, "hd128 tile shapes");
       if (do_qk) { sn[0] = f32x16{}; sn[1] = f32x16{}; }
-      if constexpr (FP8) {
-        const i32x8 pf = i32x8{pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]};
+      const i32x8 pf = i32x8{pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kb = i & 1, dc = i >> 1;
-          if (do_qk) sn[kb] = mfma8(kload8(kslot, kb, dc), qf8[dc], sn[kb]);
-          if (do_pv) o[i] = mfma8(vload8(vslot, i), pf, o[i]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kb = i & 1, dc = i >> 1, kg = i >> 2, db = i & 3;
-          if (do_qk) sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kload16(kslot, kb, dc), qf16[dc], sn[kb], 0, 0, 0);
-          if (do_pv) {
-            const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{(unsigned)pp[4 * kg], (unsigned)pp[4 * kg + 1],
-                                                                (unsigned)pp[4 * kg + 2], (unsigned)pp[4 * kg + 3]});
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vload16(vslot, kg, db), pf, o[db], 0, 0, 0);
-          }
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int kb = i & 1, dc = i >> 1;
+        if (do_qk) sn[kb] = mfma8(kload8(kslot, kb, dc), qf8[dc], sn[kb]);
+        if (do_pv) o[i] = mfma8(vload8(vslot, i), pf, o[i]);
       }
     };
-    // Softmax of one tile: P from S (e4m3fn scaled by 2^kPre, or bf16), with
-    // the checked running max; the pack happens before the check and is
-    // redone if the tile re-bases. bf16 also sums the rounded P (dot2 with
-    // (1, 1)) for the normalisation of O.
+    // Softmax of one tile: P from S (e4m3fn scaled by 2^kPre), with the
+    // checked running max; the pack happens before the check and is redone if
+    // the tile re-bases.
     // keep(): called on the rare re-base path only; the steady loop passes one
     // that uses the next tile's scores there, which keeps their MFMAs ahead of
     // the branch (inside the interleaved region) instead of sunk past it.
@@ -718,72 +684,42 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
           }
       }
       // rs: the tile's unrounded row-sum share; rx: the larger of its two 32-key
-      // block shares (the size check); rb (bf16): rs over the rounded P
-      auto expo = [&](float moff, float& rs, float& rx, float& rb) __attribute__((always_inline)) {
-        float r0 = 0.f, r1 = 0.f, b0 = 0.f, b1 = 0.f;
-        if constexpr (FP8) {
-          float gs[8];   // sums of four; a tree from these needs no zero start
+      // block shares (the size check)
+      auto expo = [&](float moff, float& rs, float& rx) __attribute__((always_inline)) {
+        float r0 = 0.f, r1 = 0.f;
+        float gs[8];   // sums of four; a tree from these needs no zero start
 #pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            const int kb = w >> 2, i = 4 * (w & 3);
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 0], c, moff));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, moff));
-            const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 2], c, moff));
-            const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 3], c, moff));
-            gs[w] = (p0 + p1) + (p2 + p3);
-            if (w == 3) r0 = (gs[0] + gs[1]) + (gs[2] + gs[3]);
-            if (w == 7) r1 = (gs[4] + gs[5]) + (gs[6] + gs[7]);
-            // the first conversion writes the low half-word only; the word of two
-            // tiles back is passed as the kept half so that nothing is cleared
-            int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[w], false);
-            pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
-          }
-        } else {
-#pragma unroll
-          for (int w = 0; w < 16; ++w) {
-            const int kg = w >> 2, kb = kg >> 1, i = 8 * (kg & 1) + 2 * (w & 3);
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 0], c, moff));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, moff));
-            const unsigned pk = pack_bf16(p0, p1);
-            pw[w] = (int)pk;
-            if (kb == 0) {
-              r0 += p0 + p1;
-              b0 = sum_bf16x2(pk, b0);
-            } else {
-              r1 += p0 + p1;
-              b1 = sum_bf16x2(pk, b1);
-            }
-          }
+        for (int w = 0; w < 8; ++w) {
+          const int kb = w >> 2, i = 4 * (w & 3);
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 0], c, moff));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 1], c, moff));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 2], c, moff));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i + 3], c, moff));
+          gs[w] = (p0 + p1) + (p2 + p3);
+          if (w == 3) r0 = (gs[0] + gs[1]) + (gs[2] + gs[3]);
+          if (w == 7) r1 = (gs[4] + gs[5]) + (gs[6] + gs[7]);
+          // the first conversion writes the low half-word only; the word of two
+          // tiles back is passed as the kept half so that nothing is cleared
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pw[w], false);
+          pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
         }
         rs = r0 + r1;
         rx = fmaxf(r0, r1);
-        rb = b0 + b1;
       };
-      float rs, rx, rb;
-      expo(moff, rs, rx, rb);
+      float rs, rx;
+      expo(moff, rs, rx);
       if constexpr (decltype(sched_c)::value) {
-        // Interleave: the MFMAs of mma() one by one, each followed by its share
-        // of the softmax VALU work and the LDS operand reads of the MFMA two
-        // places later (fp8: 8 MFMAs, 2 or 4 reads each; bf16: 32 MFMAs, 1 or 2).
+        // Interleave: the 8 MFMAs of mma() one by one, each followed by its
+        // share of the softmax VALU work and the LDS operand reads (2 or 4) of
+        // the MFMA two places later.
 #define HAT_SLOT(nds, nv)                                \
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     \
   __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);   \
   __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
-        if constexpr (FP8) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-          HAT_SLOT(2, 14) HAT_SLOT(4, 14) HAT_SLOT(2, 14) HAT_SLOT(4, 14)
-          HAT_SLOT(2, 14) HAT_SLOT(4, 14) HAT_SLOT(0, 14) HAT_SLOT(0, 14)
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-          HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4)
-          HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4)
-          HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4)
-          HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4)
-          HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4) HAT_SLOT(1, 4) HAT_SLOT(2, 4)
-          HAT_SLOT(0, 4) HAT_SLOT(0, 4)
-        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        HAT_SLOT(2, 14) HAT_SLOT(4, 14) HAT_SLOT(2, 14) HAT_SLOT(4, 14)
+        HAT_SLOT(2, 14) HAT_SLOT(4, 14) HAT_SLOT(0, 14) HAT_SLOT(0, 14)
 #undef HAT_SLOT
       }
       // In steady iterations tile 0 has given every row a finite m, so only
@@ -812,16 +748,14 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
           const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 when m was -inf
           l *= (double)alpha;
           lf *= alpha;
-          if constexpr (!FP8) dl *= alpha;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) o[db] *= alpha;
           m = mnew;
           moff = kPre - (m == -INFINITY ? 0.f : m);
-          expo(moff, rs, rx, rb);
+          expo(moff, rs, rx);
         }
       }
       lf += rs;
-      if constexpr (!FP8) dl += rb - rs;
     };
 
     // The wave's bounds, made provably wave-uniform so that the loops below
