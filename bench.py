@@ -215,7 +215,9 @@ def bench_workload(args, w, make_inputs):
     dev = torch.device("cuda:0")
     fmt = "bf16" if w.fmt in ("f32", "bf16") else w.fmt
     inp = make_inputs(w, fmt)
-    causal = bool(w.causal[-1])
+    causal = bool(w.causal[-1]) and not args.non_causal
+    if args.non_causal and False not in w.causal:
+        raise SystemExit(f"--non-causal: workload {w.name} is defined causal only")
 
     def put(a):
         t = torch.from_numpy(np.ascontiguousarray(a))
@@ -666,6 +668,8 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="time one other workload of synth.WORKLOADS instead (a context line, not the "
                          "headline); causal workloads run causal")
+    ap.add_argument("--non-causal", action="store_true",
+                    help="with --workload: run a workload defined both ways (llm) without the causal mask")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: the attention path runs on one GPU only (no sharding or collectives); use --gpus 1",
