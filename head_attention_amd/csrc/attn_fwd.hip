@@ -787,6 +787,16 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       softmax(sc, pc, std::false_type{}, u, std::true_type{}, keep);
     };
 
+    // A steady iteration whose ring slots and synchronisation are decided at
+    // run time (the short runs after the eight-at-a-time loop).
+    auto steady_rt = [&](int u, f32x16 (&sc)[NKB], f32x16 (&sn)[NKB], int (&pc)[NPW], const int (&pp)[NPW])
+        __attribute__((always_inline)) {
+      if (u % kSync == 0) psync(u);
+      mma(sn, pp, (u + 1) % NS, (u + NS - 1) % NS, true, true);
+      auto keep = [&]() __attribute__((always_inline)) { asm volatile("" ::"v"(sn[0]), "v"(sn[1])); };
+      softmax(sc, pc, std::false_type{}, u, std::true_type{}, keep);
+    };
+
     // Prologue: K(0 .. kSync) and V(0 .. kSync-2), then S(0); iteration 0
     // queues the next ones.
 #pragma unroll
@@ -814,6 +824,14 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
         steady(u + 5, S[0], S[1], P[0], P[1], 7, 5, no);
         steady(u + 6, S[1], S[0], P[1], P[0], 0, 6, no);
         steady(u + 7, S[0], S[1], P[0], P[1], 1, 7, yes);   // u + 7 = 0 mod 8
+        flush();
+      }
+      // Fewer than eight steady iterations left (all of a short key range):
+      // two at a time, interleaved as above, with the ring slots and the
+      // synchronisation decided at run time (u stays odd).
+      for (; u + 1 < ss_end; u += 2) {
+        steady_rt(u, S[1], S[0], P[1], P[0]);
+        steady_rt(u + 1, S[0], S[1], P[0], P[1]);
         flush();
       }
       // The rest (u is odd here), two at a time with compile-time buffers.
