@@ -43,7 +43,9 @@
 //    epilogue divides by l and multiplies by v_descale, so the factor cancels.
 //  * Causal: a workgroup only loads the key tiles its rows can see; within
 //    them a wave skips tiles entirely above its rows and masks only tiles that
-//    cross its diagonal. Causal grids run the longest query tiles first.
+//    cross its diagonal. Causal grids run the longest query tiles first; a
+//    causal grid of key-split workgroups (one round) pairs an early and a late
+//    64-row block in each workgroup instead, so that all take about as long.
 //  * Local attention (window sides and sink keys; the window_size_left /
 //    window_size_right arguments of the page "F8 fmha ASM gfx950", Test
 //    Result section): a workgroup loads only the sink tiles and the tiles its
@@ -130,13 +132,15 @@ template <int D, bool CAUSAL, bool FP8, bool WIN, int NW, bool KS>
 __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   constexpr int kW = NW;            // waves per workgroup (8, or 4 for grids that leave CUs idle)
   constexpr int kThr = 64 * NW;
-  // KS (key split, bf16 without a window): waves w and w + NW/2 own the same
-  // 32 rows and take alternate key tiles, two tiles per barrier step; their
-  // (m, l, O) are merged through LDS at the end. A workgroup then covers
-  // 32 NW/2 rows at two waves per SIMD, for grids too small to fill the CUs.
+  // KS (key split, bf16 without a window): two waves own the same 32 rows
+  // (waves w and w + NW/2; causal: 2r and 2r + 1) and take alternate key
+  // tiles, two tiles per barrier step; their (m, l, O) are merged through LDS
+  // at the end. A workgroup then covers 32 NW/2 rows at two waves per SIMD,
+  // for grids too small to fill the CUs.
   static_assert(!KS || (!FP8 && !WIN && NW == 8), "the key split is a bf16 8-wave mode");
   constexpr int kRG = KS ? NW / 2 : NW;   // waves with distinct query rows
   constexpr int kRows = 32 * kRG;         // query rows per workgroup
+  constexpr bool FOLD = KS && CAUSAL;     // folded causal grid (below)
   using T = Tile<D, FP8>;
   constexpr int ROWB = T::ROWB;
   constexpr int NDB = D / 32;                       // 32-wide output column blocks
@@ -177,8 +181,8 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     bid = gb % per_split;
   }
   int bh, qt;
-  if (CAUSAL) {  // longest rows first
-    qt = p.n_qtiles - 1 - bid / BH;
+  if (CAUSAL) {  // longest rows first (folded: the workgroups whose later block reaches furthest)
+    qt = FOLD ? bid / BH : p.n_qtiles - 1 - bid / BH;
     // Within one query-tile row of the grid, workgroup r goes to XCD r % 8:
     // when the heads split evenly over the XCDs, give XCD x the contiguous
     // heads [x BH/8, (x+1) BH/8), which share key/value heads under grouped
@@ -195,10 +199,21 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   const int kv_start = p.kv_start + s0;
   const int b = bh / p.Hq, h = bh % p.Hq, hk = h / p.group;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rw = KS ? wave % kRG : wave;   // the wave's 32-row group
-  [[maybe_unused]] const int kh = KS ? wave / kRG : 0;   // KS: its key half (tiles kh, kh + 2, ...)
+  // KS and causal: the grid is folded. Workgroup qt takes the 64-row blocks qt
+  // (row groups 0, 1) and J-1-qt (row groups 2, 3) of the head's J blocks, so
+  // that every workgroup holds about the same number of visible (query, key)
+  // pairs and the grid's one round ends together instead of waiting on the
+  // last rows' workgroup. The two key halves of a row group are waves 2r', 2r'+1
+  // (r' = row group mod 2), so that waves w and w + 4, which share a SIMD, hold
+  // one row group of each block. When J is odd the middle workgroup's second
+  // block is its first, and row groups 2, 3 stay idle.
+  const int rw = !KS ? wave : FOLD ? ((wave >> 2) << 1) | ((wave >> 1) & 1) : wave % kRG;   // the wave's 32-row group
+  [[maybe_unused]] const int kh = !KS ? 0 : FOLD ? wave & 1 : wave / kRG;   // KS: its key half (tiles kh, kh + 2, ...)
   const int g = lane >> 5, n = lane & 31;
-  const int q0 = qt * kRows, qw = q0 + rw * 32, qi = qw + n;
+  const int nblk = (p.Sq + 63) >> 6;   // FOLD: the head's 64-row blocks
+  const int q0 = FOLD ? 64 * (nblk - 1 - qt) : qt * kRows;   // FOLD: the second (later) block
+  const int qw = FOLD ? 64 * (rw < 2 ? qt : nblk - 1 - qt) + 32 * (rw & 1) : q0 + rw * 32, qi = qw + n;
+  const bool fold_dup = FOLD && rw >= 2 && nblk - 1 - qt == qt;
 
   const size_t qrow0 = (size_t)(b * p.Hq + h) * (size_t)p.Sq;
   const size_t krow0 = (size_t)(b * p.Hkv + hk) * (size_t)p.Skv + (size_t)(Skv > 0 ? s0 : 0);
@@ -219,10 +234,10 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   const float smask = cneg ? INFINITY : -INFINITY;
 
   // Key tiles this workgroup needs, and those this wave needs.
-  const int rows_end = min(q0 + kRows, p.Sq);
+  const int rows_end = min(q0 + (FOLD ? 64 : kRows), p.Sq);
   const int kv_end = CAUSAL ? min(Skv, max(0, rows_end - kv_start)) : Skv;
   const int ntiles = (kv_end + kBN - 1) / kBN;
-  const bool wave_live = qw < p.Sq;
+  const bool wave_live = qw < p.Sq && !fold_dup;
   const int w_kv_end = CAUSAL ? min(Skv, max(0, min(qw + 32, p.Sq) - kv_start)) : Skv;
   const int w_ntiles = wave_live ? (w_kv_end + kBN - 1) / kBN : 0;
 
@@ -265,18 +280,22 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     }
   }
 
-  // Q has landed before any copy is queued behind it: the compiler's own
-  // memory-counter waits for Q then never wait for the copies.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-
-  // Clear all of LDS once (both rings), so that the rows of a ragged last
-  // key tile never expose uninitialised LDS. With whole tiles only, every
-  // byte the loop reads is written by a tile copy first, and the clear is
-  // skipped (the condition is the workgroup's own).
-  if (Skv % kBN != 0)
-    for (int i = threadIdx.x; i < kLds / 16; i += kThr)
-      *(LDS_AS u32x4*)(smem + i * 16) = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
+  // Wait for Q, then clear all of LDS once (both rings) when the last key
+  // tile is ragged, so that its missing rows never expose uninitialised LDS.
+  // With whole tiles only, every byte the loop reads is written by a tile
+  // copy first, and the clear is skipped (the condition is the workgroup's
+  // own). The wait is the compiler's own instruction, so its memory-counter
+  // bookkeeping knows that Q has landed, and none of its later waits waits
+  // for a copy queued behind Q.
+  const bool ragged = Skv % kBN != 0;
+  auto q_wait_and_clear = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if (ragged)
+      for (int i = threadIdx.x; i < kLds / 16; i += kThr)
+        *(LDS_AS u32x4*)(smem + i * 16) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  };
+  if constexpr (!KS) q_wait_and_clear();
 
   // Global -> LDS for tile t into slot t % kStages: the 2*NINSTR 1-KB pieces
   // (K first, then V) are split evenly, piece w*PW .. w*PW+PW-1 to wave w. LDS
@@ -307,6 +326,21 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       dma16(isv ? rvw : rkw, goff, dst);
     }
   };
+  // The key-split loop waits for every copy in flight before its first tile
+  // anyway: with whole tiles only (no clear), it queues its first two tiles
+  // right behind the Q loads, and one wait covers both (a memory latency less
+  // at each workgroup's start, which these one-round grids see whole). The
+  // other loops first wait for tile 0 alone and queue their copies after Q
+  // has landed (queued before, they made the many-round grids 2-4 % slower).
+  if constexpr (KS) {
+    auto first = [&]() __attribute__((always_inline)) {
+      if (ntot > 0) issue(0);
+      if (ntot > 1) issue(1);
+    };
+    if (!ragged) first();
+    q_wait_and_clear();
+    if (ragged) first();
+  }
 
   f32x16 o[NDB];
 #pragma unroll
@@ -848,8 +882,6 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     // steps (ntot is the workgroup's), so the barriers pair up.
     const int first_masked = CAUSAL ? min(Skv / kBN, max(0, qw - kv_start + 1) / kBN) : Skv / kBN;
     const int n_plain = min(first_masked, ntot);
-    if (ntot > 0) issue(0);
-    if (ntot > 1) issue(1);
     auto ksync = [&](int v) __attribute__((always_inline)) {
       wait_vmcnt<0>();
       __syncthreads();

@@ -301,9 +301,13 @@ def _with_k(inp, k32):
 def test_key_split_workgroups(D, causal):
     """A bf16 grid that fills at most half the CUs runs as 8-wave workgroups of 128
     rows in which two waves share each 32 rows and take alternate key tiles, merged
-    at the end. Shapes with an odd and an even number of key tiles, a ragged key
-    tail, grouped heads and rows past Sq in the last tile; against the oracle."""
-    for (B, Hq, Hkv, Sq, Skv) in ((1, 4, 2, 700, 1050), (2, 2, 1, 300, 1280)):
+    at the end. Causal grids pair 64-row block j with block J-1-j in one workgroup:
+    odd J (700, 300 rows: the middle workgroup holds one block), even J with whole
+    blocks (1024) and with a ragged last block (1000). Shapes with an odd and an even
+    number of key tiles, a ragged key tail, grouped heads and rows past Sq in the
+    last tile; against the oracle."""
+    for (B, Hq, Hkv, Sq, Skv) in ((1, 4, 2, 700, 1050), (2, 2, 1, 300, 1280), (1, 3, 3, 1024, 1024),
+                                  (1, 2, 2, 1000, 1000)):
         say(f"case key split D={D} causal={causal} B{B} H{Hq}/{Hkv} {Sq}x{Skv}")
         inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, "bf16", seed=71 + D + causal + Sq)
         scale = 1 / math.sqrt(D)
