@@ -299,9 +299,9 @@ def bench_workload(args, w, make_inputs):
         "ms_p95": round(float(np.percentile(tl, 95)) * 1e3, 4), "ms_min": round(float(tl.min()) * 1e3, 4),
         "ms_loop100": round(t_loop * 1e3, 4), "tflops_loop100": round(flops / t_loop / 1e12, 2),
         "frac_of_peak": round(tf / PEAK_TFLOPS[dtn], 4), "key_splits": nsplit if nsplit is not None else 1,
-        # the library's grid for an unsplit call: 256-row workgroups, or 128-row ones
-        # (twice as many) when the 256-row grid would fill at most half the CUs
-        **grid_of(w, nsplit),
+        # the library's grid for an unsplit call: 256-row workgroups, or smaller ones
+        # when the 256-row grid would fill at most half the CUs
+        **grid_of(w, nsplit, fmt == "bf16" and not local),
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS[dtn], "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_TFLOPS[dtn], 4), "traffic": None,
                      "kernel": f"attn_fwd_kernel<{w.D},{str(causal).lower()},{str(dtn == 'fp8').lower()},"
@@ -410,16 +410,20 @@ SWEEP_SPLIT = [  # B, H, Sq, Skv, D, dtype: few query tiles against long key ran
 ]
 
 
-def grid_of(w, nsplit):
+def grid_of(w, nsplit, key_split):
     """Workgroups and rows per workgroup of an unsplit call (None for split calls,
-    whose grid the library sizes from the key splits)."""
+    whose grid the library sizes from the key splits), as the library chooses them:
+    256-row workgroups; when those fill at most half the CUs, 128-row ones, or for
+    bf16 without a window (key_split) 64-row ones where that grid still fits one
+    round of the CUs."""
     import torch
     if nsplit not in (None, 1):
         return {"workgroups": None, "rows_per_workgroup": None}
     tiles = w.B * w.Hq * ((w.Sq + 255) // 256)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if 2 * tiles <= cus:
-        return {"workgroups": w.B * w.Hq * ((w.Sq + 127) // 128), "rows_per_workgroup": 128}
+        rows = 64 if key_split and w.B * w.Hq * ((w.Sq + 63) // 64) <= cus else 128
+        return {"workgroups": w.B * w.Hq * ((w.Sq + rows - 1) // rows), "rows_per_workgroup": rows}
     return {"workgroups": tiles, "rows_per_workgroup": 256}
 
 

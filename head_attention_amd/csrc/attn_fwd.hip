@@ -128,19 +128,22 @@ struct Tile {
   }
 };
 
-template <int D, bool CAUSAL, bool FP8, bool WIN, int NW, bool KS>
+template <int D, bool CAUSAL, bool FP8, bool WIN, int NW, int KS>
 __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   constexpr int kW = NW;            // waves per workgroup (8, or 4 for grids that leave CUs idle)
   constexpr int kThr = 64 * NW;
-  // KS (key split, bf16 without a window): two waves own the same 32 rows
-  // (waves w and w + NW/2; causal: 2r and 2r + 1) and take alternate key
-  // tiles, two tiles per barrier step; their (m, l, O) are merged through LDS
-  // at the end. A workgroup then covers 32 NW/2 rows at two waves per SIMD,
-  // for grids too small to fill the CUs.
+  // KS (key split, bf16 without a window; 0 = none): KS waves own the same 32
+  // rows and share its key tiles, two tiles per barrier step, and their (m,
+  // l, O) are merged through LDS at the end. KS = 2: waves w and w + NW/2
+  // (causal: 2r and 2r + 1) take alternate tiles. KS = 4: waves 2j + r (j =
+  // 0..3) of row group r each take one 32-key half of one of the step's two
+  // tiles (tile j / 2, half j % 2). A workgroup then covers 32 NW / KS rows
+  // at two waves per SIMD, for grids too small to fill the CUs.
+  static_assert(KS == 0 || KS == 2 || KS == 4, "key split factors 2 and 4");
   static_assert(!KS || (!FP8 && !WIN && NW == 8), "the key split is a bf16 8-wave mode");
-  constexpr int kRG = KS ? NW / 2 : NW;   // waves with distinct query rows
+  constexpr int kRG = KS ? NW / KS : NW;  // waves with distinct query rows
   constexpr int kRows = 32 * kRG;         // query rows per workgroup
-  constexpr bool FOLD = KS && CAUSAL;     // folded causal grid (below)
+  constexpr bool FOLD = KS == 2 && CAUSAL;   // folded causal grid (below)
   using T = Tile<D, FP8>;
   constexpr int ROWB = T::ROWB;
   constexpr int NDB = D / 32;                       // 32-wide output column blocks
@@ -207,8 +210,9 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   // (r' = row group mod 2), so that waves w and w + 4, which share a SIMD, hold
   // one row group of each block. When J is odd the middle workgroup's second
   // block is its first, and row groups 2, 3 stay idle.
-  const int rw = !KS ? wave : FOLD ? ((wave >> 2) << 1) | ((wave >> 1) & 1) : wave % kRG;   // the wave's 32-row group
-  [[maybe_unused]] const int kh = !KS ? 0 : FOLD ? wave & 1 : wave / kRG;   // KS: its key half (tiles kh, kh + 2, ...)
+  const int rw = !KS ? wave : KS == 4 ? wave & 1 : FOLD ? ((wave >> 2) << 1) | ((wave >> 1) & 1) : wave % kRG;   // the wave's 32-row group
+  // KS: its share of the keys, 0 .. KS-1 (KS = 2: tiles kh, kh + 2, ...)
+  [[maybe_unused]] const int kh = !KS ? 0 : KS == 4 ? wave >> 1 : FOLD ? wave & 1 : wave / kRG;
   const int g = lane >> 5, n = lane & 31;
   const int nblk = (p.Sq + 63) >> 6;   // FOLD: the head's 64-row blocks
   const int q0 = FOLD ? 64 * (nblk - 1 - qt) : qt * kRows;   // FOLD: the second (later) block
@@ -387,7 +391,12 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   // speculated on them.
   // slot_c: the tile's ring slot as a compile-time constant (its LDS operand
   // reads then take immediate offsets), or kAnySlot for u % kStages.
-  auto step = [&](int u, auto masked_c, auto slot_c) __attribute__((always_inline)) {
+  // nkb_c: the 32-key blocks taken, kb0 .. kb0 + NB - 1 (NB = NKB: the whole
+  // tile, kb0 = 0; NB = 1: a half tile, bf16 only). The LDS swizzles do not
+  // depend on the block, so a half only shifts the rows read.
+  auto stepk = [&](int u, auto masked_c, auto slot_c, auto nkb_c, int kb0) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nkb_c)::value;
+    static_assert(NB == NKB || (NB == 1 && !FP8), "half tiles are a bf16 form");
     const int t = tile_of(u);
     constexpr int kSlot = decltype(slot_c)::value;
     const int slot = kSlot >= 0 ? kSlot : u % kStages;
@@ -395,10 +404,11 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     const LDS_AS char* vs = smem + (slot * 2 + 1) * T::BYTES;
 
     // ---- S^T = K Q^T ----
-    f32x16 s[NKB];
+    f32x16 s[NB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
+    for (int kk = 0; kk < NB; ++kk) {
+      const int kb = kb0 + kk;
+      s[kk] = f32x16{};
       const int r = 32 * kb + krow;
       const LDS_AS char* krowp = ks + r * ROWB;
       if constexpr (!FP8) {
@@ -406,7 +416,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
         for (int dc = 0; dc < D / 16; ++dc) {
           const int lc = 2 * dc + g;
           const bf16x8 kf = *(const LDS_AS bf16x8*)(krowp + ((lc ^ T::kswz(r)) * 16));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf16[dc], s[kb], 0, 0, 0);
+          s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf16[dc], s[kk], 0, 0, 0);
         }
       } else {
 #pragma unroll
@@ -415,7 +425,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
           const i32x4 k0 = *(const LDS_AS i32x4*)(krowp + ((lc ^ T::kswz(r)) * 16));
           const i32x4 k1 = *(const LDS_AS i32x4*)(krowp + (((lc + 1) ^ T::kswz(r)) * 16));
           const i32x8 kf = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf8[dc], s[kb], 0, 0, 0, 127, 0, 127);
+          s[kk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf8[dc], s[kk], 0, 0, 0, 127, 0, 127);
         }
       }
     }
@@ -424,14 +434,14 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     if constexpr (decltype(masked_c)::value) {
       const int key0 = t * kBN;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int kk = 0; kk < NB; ++kk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+          const int key = key0 + 32 * (kb0 + kk) + 8 * (i >> 2) + 4 * g + (i & 3);
           const int kp = key + kv_start;
           bool ok = key < Skv && (!CAUSAL || kp <= qi);
           if constexpr (WIN) ok = ok && ((kp >= qi - wl && kp <= qi + wr) || kp < sink);
-          s[kb][i] = ok ? s[kb][i] : smask;
+          s[kk][i] = ok ? s[kk][i] : smask;
         }
     }
 
@@ -444,13 +454,13 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     // Otherwise (or while m is still -inf) the tile's row max is taken and, if
     // it exceeds m in any row, m becomes the exact running max, O and l are
     // rescaled, and p is formed again.
-    f32x16 sraw[NKB];
+    f32x16 sraw[NB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sraw[kb] = s[kb];
+    for (int kb = 0; kb < NB; ++kb) sraw[kb] = s[kb];
     float moff = kPre - (m == -INFINITY ? 0.f : m);
-    float rk[NKB];
+    float rk[NB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, moff));
@@ -459,7 +469,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       }
     float rs = rk[0], rx = rk[0];
 #pragma unroll
-    for (int kb = 1; kb < NKB; ++kb) {
+    for (int kb = 1; kb < NB; ++kb) {
       rs += rk[kb];
       rx = fmaxf(rx, rk[kb]);
     }
@@ -467,12 +477,12 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       float mx = -INFINITY;   // max of s, or of -s when c < 0
       if (!cneg) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sraw[kb][i]);
       } else {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, -sraw[kb][i]);
       }
@@ -489,7 +499,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
         moff = kPre - (m == -INFINITY ? 0.f : m);
         rs = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sraw[kb][i], c, moff));
@@ -505,7 +515,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       const int rr = l16 >> 2, ss = l16 & 3;
       float dr = -rs;   // becomes sum(bf16(p)) - sum(p) over this tile
 #pragma unroll
-      for (int kg = 0; kg < kBN / 16; ++kg) {  // 16-key groups
+      for (int kg = 0; kg < 2 * NB; ++kg) {  // 16-key groups
         const int kb = kg >> 1, half = kg & 1;
         bf16x8 pf;
         {
@@ -517,7 +527,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) dr = sum_bf16x2(pk[w], dr);
         }
-        const int key1 = 32 * kb + 16 * half + 4 * g + rr;   // keys key1, key1+8
+        const int key1 = 32 * (kb0 + kb) + 16 * half + 4 * g + rr;   // keys key1, key1+8
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int col = 32 * db + 16 * dgrp + 4 * ss;
@@ -565,6 +575,9 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
         }
       }
     }
+  };
+  auto step = [&](int u, auto masked_c, auto slot_c) __attribute__((always_inline)) {
+    stepk(u, masked_c, slot_c, std::integral_constant<int, NKB>{}, 0);
   };
   if constexpr (PIPE) {
     // ---- software-pipelined tile loop ----
@@ -876,12 +889,20 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       }
     }
   } else if constexpr (KS) {
-    // Tiles 2v and 2v+1 (slots 2v % kStages and (2v+1) % kStages) at step v,
-    // by the waves of key half 0 and 1; step v's barrier retires the slots of
-    // step v-1, which take tiles 2v+2 and 2v+3. Every wave runs ceil(ntot/2)
-    // steps (ntot is the workgroup's), so the barriers pair up.
+    // Tiles 2v and 2v+1 (slots 2v % kStages and (2v+1) % kStages) at step v:
+    // KS = 2, by the waves of key share 0 and 1; KS = 4, tile 2v + kh / 2 by
+    // the two waves kh of that tile, each taking its half kh % 2 of the keys.
+    // Step v's barrier retires the slots of step v-1, which take tiles 2v+2
+    // and 2v+3. Every wave runs ceil(ntot/2) steps (ntot is the workgroup's),
+    // so the barriers pair up.
     const int first_masked = CAUSAL ? min(Skv / kBN, max(0, qw - kv_start + 1) / kBN) : Skv / kBN;
     const int n_plain = min(first_masked, ntot);
+    const int kt = KS == 4 ? kh >> 1 : kh;          // the wave's tile of each step
+    [[maybe_unused]] const int kb0 = kh & 1;        // KS = 4: its half of that tile
+    auto kstep = [&](int u, auto masked_c) __attribute__((always_inline)) {
+      if constexpr (KS == 4) stepk(u, masked_c, kAnySlot, std::integral_constant<int, 1>{}, kb0);
+      else step(u, masked_c, kAnySlot);
+    };
     auto ksync = [&](int v) __attribute__((always_inline)) {
       wait_vmcnt<0>();
       __syncthreads();
@@ -891,21 +912,25 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
     int v = 0;
     for (; 2 * v + 1 < n_plain; ++v) {   // both tiles of the step unmasked for this wave's rows
       ksync(v);
-      if (2 * v + kh < w_ntiles) step(2 * v + kh, std::false_type{}, kAnySlot);
+      if (2 * v + kt < w_ntiles) kstep(2 * v + kt, std::false_type{});
     }
     for (; 2 * v < ntot; ++v) {
       ksync(v);
-      const int u = 2 * v + kh;
-      if (u < ntot && u < w_ntiles) step(u, std::true_type{}, kAnySlot);
+      const int u = 2 * v + kt;
+      // (KS = 4: a half holding no key the wave's rows may see is skipped)
+      if (u < ntot && u < w_ntiles && (KS != 4 || kBN * u + 32 * kb0 < w_kv_end)) kstep(u, std::true_type{});
     }
-    // Merge: key half 1 hands its m, l, dl and O (lane by lane: the same rows
-    // and columns) to key half 0 through LDS; half 0 then writes the output.
+    // Merge: key shares 1 .. KS-1 hand their m, l, dl and O (lane by lane: the
+    // same rows and columns) to share 0 through LDS; share 0 then writes the
+    // output.
     wait_vmcnt<0>();
     __syncthreads();   // every ring read done
     constexpr int NF = NDB * 16 + 4;   // floats per lane: O, m, dl, l (two words)
-    static_assert(kRG * NF * 64 * 4 <= kLds, "merge buffer fits the ring");
-    LDS_AS float* xb = (LDS_AS float*)smem + rw * NF * 64 + lane;
-    if (kh == 1) {
+    constexpr int NP = KS - 1;         // partials per row group
+    static_assert(kRG * NP * NF * 64 * 4 <= kLds, "merge buffer fits the ring");
+    LDS_AS float* xb0 = (LDS_AS float*)smem + rw * NP * NF * 64 + lane;
+    if (kh != 0) {
+      LDS_AS float* xb = xb0 + (kh - 1) * NF * 64;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -917,20 +942,55 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       xb[(NF - 1) * 64] = __uint_as_float(lw[1]);
     }
     __syncthreads();
-    if (kh == 1) return;
-    const float m1 = xb[(NF - 4) * 64], dl1 = xb[(NF - 3) * 64];
-    const double l1 = __builtin_bit_cast(double, u32x2{__float_as_uint(xb[(NF - 2) * 64]),
-                                                       __float_as_uint(xb[(NF - 1) * 64])});
-    const float mm = fmaxf(m, m1);
-    const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
-    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+    if (kh != 0) return;
+    if constexpr (KS == 2) {
+      LDS_AS float* xb = xb0;
+      const float m1 = xb[(NF - 4) * 64], dl1 = xb[(NF - 3) * 64];
+      const double l1 = __builtin_bit_cast(double, u32x2{__float_as_uint(xb[(NF - 2) * 64]),
+                                                         __float_as_uint(xb[(NF - 1) * 64])});
+      const float mm = fmaxf(m, m1);
+      const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] = o[db][i] * a0 + xb[(db * 16 + i) * 64] * a1;
-    l = l * (double)a0 + l1 * (double)a1;
-    dl = dl * a0 + dl1 * a1;
-    m = mm;
+        for (int i = 0; i < 16; ++i) o[db][i] = o[db][i] * a0 + xb[(db * 16 + i) * 64] * a1;
+      l = l * (double)a0 + l1 * (double)a1;
+      dl = dl * a0 + dl1 * a1;
+      m = mm;
+    } else {   // KS = 4: the three partners' partials, under the largest of the four maxima
+      float mj[NP], aj[NP];
+      float mm = m;
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        mj[j] = xb0[(j * NF + NF - 4) * 64];
+        mm = fmaxf(mm, mj[j]);
+      }
+      const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+#pragma unroll
+      for (int j = 0; j < NP; ++j) aj[j] = mj[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj[j] - mm);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float acc = o[db][i] * a0;
+#pragma unroll
+          for (int j = 0; j < NP; ++j) acc += xb0[(j * NF + db * 16 + i) * 64] * aj[j];
+          o[db][i] = acc;
+        }
+      double lacc = l * (double)a0;
+      float dacc = dl * a0;
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const double lj = __builtin_bit_cast(double, u32x2{__float_as_uint(xb0[(j * NF + NF - 2) * 64]),
+                                                           __float_as_uint(xb0[(j * NF + NF - 1) * 64])});
+        lacc += lj * (double)aj[j];
+        dacc += xb0[(j * NF + NF - 3) * 64] * aj[j];
+      }
+      l = lacc;
+      dl = dacc;
+      m = mm;
+    }
   } else if constexpr (!WIN) {
     const int first_masked = CAUSAL ? min(Skv / kBN, max(0, qw - kv_start + 1) / kBN) : Skv / kBN;
     const int n_plain = min(first_masked, ntot);
@@ -1117,15 +1177,18 @@ typedef void (*kernel_fn)(Params);
 template <int D, bool FP8, int NW>
 kernel_fn pick_nw(bool causal, bool win) {
   if (win)
-    return causal ? attn_fwd_kernel<D, true, FP8, true, NW, false> : attn_fwd_kernel<D, false, FP8, true, NW, false>;
-  return causal ? attn_fwd_kernel<D, true, FP8, false, NW, false> : attn_fwd_kernel<D, false, FP8, false, NW, false>;
+    return causal ? attn_fwd_kernel<D, true, FP8, true, NW, 0> : attn_fwd_kernel<D, false, FP8, true, NW, 0>;
+  return causal ? attn_fwd_kernel<D, true, FP8, false, NW, 0> : attn_fwd_kernel<D, false, FP8, false, NW, 0>;
 }
 
-// ks: the bf16 key-split instance (8 waves, 128 rows); nw otherwise.
+// ks: the bf16 key-split factor (8 waves; 2: 128 rows, 4: 64 rows), 0 for
+// none; nw otherwise.
 template <int D, bool FP8>
-kernel_fn pick(bool causal, bool win, int nw, bool ks) {
-  if constexpr (!FP8)
-    if (ks) return causal ? attn_fwd_kernel<D, true, false, false, 8, true> : attn_fwd_kernel<D, false, false, false, 8, true>;
+kernel_fn pick(bool causal, bool win, int nw, int ks) {
+  if constexpr (!FP8) {
+    if (ks == 4) return causal ? attn_fwd_kernel<D, true, false, false, 8, 4> : attn_fwd_kernel<D, false, false, false, 8, 4>;
+    if (ks == 2) return causal ? attn_fwd_kernel<D, true, false, false, 8, 2> : attn_fwd_kernel<D, false, false, false, 8, 2>;
+  }
   return nw == 4 ? pick_nw<D, FP8, 4>(causal, win) : pick_nw<D, FP8, 8>(causal, win);
 }
 
@@ -1191,10 +1254,17 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   // grid of 256-row tiles fills at most half the CUs, so that the doubled grid
   // of half-size workgroups still runs in one round.
   const int nw = nsp == 1 && 2 * B * Hq * ((Sq + kBM - 1) / kBM) <= (int64_t)device_cus() ? 4 : 8;
-  // bf16 without a window runs those 128-row tiles as 8-wave key-split
-  // workgroups instead (two waves per row group, alternate key tiles).
-  const bool ks = nw == 4 && dtype == ATTN_BF16 && !win;
-  const int64_t n_qtiles = (Sq + 32 * nw - 1) / (32 * nw);
+  // bf16 without a window runs 8-wave key-split workgroups instead: of 64
+  // rows (four waves per row group, each on half of one of a step's two key
+  // tiles) when that grid still fits one round of the CUs, else of 128 rows
+  // (two waves per row group taking alternate tiles). Measured at D128
+  // causal: 64-row workgroups take 14-16 % off a grid that fits one round;
+  // in two rounds they are 8 % slower than one round of 128-row workgroups
+  // (their short steps expose the copies' latency).
+  const int ks = nw == 4 && dtype == ATTN_BF16 && !win
+                     ? (B * Hq * ((Sq + 63) / 64) <= (int64_t)device_cus() ? 4 : 2) : 0;
+  const int64_t rows_wg = ks ? 32 * 8 / ks : 32 * nw;   // query rows per workgroup
+  const int64_t n_qtiles = (Sq + rows_wg - 1) / rows_wg;
   const int64_t rows = B * Hq * Sq;
   const int64_t ntiles = B * Hq * n_qtiles;
   int64_t n_full = -1, part_rows = rows, part_row0 = 0, grid = ntiles * nsp;
@@ -1202,7 +1272,7 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
     const int64_t cus = device_cus();
     n_full = ntiles / cus * cus;
     if (n_full == 0 || n_full == ntiles) return ATTN_ERR_SHAPE;
-    part_row0 = (n_full / n_qtiles) * Sq + (n_full % n_qtiles) * (32 * nw);
+    part_row0 = (n_full / n_qtiles) * Sq + (n_full % n_qtiles) * rows_wg;
     part_rows = rows - part_row0;
     grid = n_full + (ntiles - n_full) * nsp;
   }
@@ -1246,7 +1316,7 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
 
   kernel_fn fn;
   if (dtype == ATTN_BF16) fn = D == 128 ? pick<128, false>(causal, win, nw, ks) : pick<64, false>(causal, win, nw, ks);
-  else fn = D == 128 ? pick<128, true>(causal, win, nw, false) : pick<64, true>(causal, win, nw, false);
+  else fn = D == 128 ? pick<128, true>(causal, win, nw, 0) : pick<64, true>(causal, win, nw, 0);
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(ks ? 512 : 64 * nw), 0, (hipStream_t)stream, p);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   if (nsp > 1) {

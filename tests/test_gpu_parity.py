@@ -299,15 +299,17 @@ def _with_k(inp, k32):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_key_split_workgroups(D, causal):
-    """A bf16 grid that fills at most half the CUs runs as 8-wave workgroups of 128
-    rows in which two waves share each 32 rows and take alternate key tiles, merged
-    at the end. Causal grids pair 64-row block j with block J-1-j in one workgroup:
-    odd J (700, 300 rows: the middle workgroup holds one block), even J with whole
-    blocks (1024) and with a ragged last block (1000). Shapes with an odd and an even
-    number of key tiles, a ragged key tail, grouped heads and rows past Sq in the
-    last tile; against the oracle."""
+    """A bf16 grid that fills at most half the CUs runs as 8-wave key-split
+    workgroups, merged at the end: of 64 rows, four waves per 32 rows each taking
+    half of one of a step's two key tiles, while that grid fits one round of the
+    CUs (the first four shapes); else of 128 rows, two waves per 32 rows taking
+    alternate tiles (the last two: 16 heads of 2000 and 2048 rows). Causal 128-row
+    grids pair 64-row block j with block J-1-j in one workgroup (J = 32 here, the
+    last block ragged at 2000 rows). Shapes with an odd and an even number of key
+    tiles, a ragged key tail, grouped heads, rows past Sq in the last tile, an odd
+    block count (700, 300 rows) and whole blocks (1024); against the oracle."""
     for (B, Hq, Hkv, Sq, Skv) in ((1, 4, 2, 700, 1050), (2, 2, 1, 300, 1280), (1, 3, 3, 1024, 1024),
-                                  (1, 2, 2, 1000, 1000)):
+                                  (1, 2, 2, 1000, 1000), (1, 16, 4, 2000, 2100), (2, 8, 8, 2048, 2048)):
         say(f"case key split D={D} causal={causal} B{B} H{Hq}/{Hkv} {Sq}x{Skv}")
         inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, "bf16", seed=71 + D + causal + Sq)
         scale = 1 / math.sqrt(D)
