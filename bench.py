@@ -7,7 +7,9 @@ One step is the whole hot path over one batch: the bf16 forward at
 B1 H5 S75600 D128 (non-causal) and the fp8 (e4m3fn, per-tensor descale)
 forward at the same shape, each writing O (bf16) and LSE (fp32). Inputs are
 seeded synthetic N(0,1) draws (fp8: per-tensor amax/448 quantisation), already
-resident in HBM when timing starts. Prints ONE JSON line.
+resident in HBM when timing starts. Warm-up is at least W steps and at least half
+a second of back-to-back launches (``warmup_launches`` in the line), so that the
+timed steps see the GPU's settled clock. Prints ONE JSON line.
 
 Throughput uses the pages' attention-forward convention, 4*B*H*Sq*Skv*D flops
 per launch (halved for causal); ``attn_tflops`` and ``pages_gbps`` reproduce
@@ -207,6 +209,27 @@ def cpu_baseline_backward(q, k, v, do, w, causal, budget_s):
                       f"{_cpu_model()})"}
 
 
+def warm_up(launch, n, min_seconds=0.5):
+    """Untimed launches before a timed region: at least n, and back to back for at
+    least min_seconds of wall time. The GPU's clock climbs over the first stretch of
+    load (a 0.037 ms launch timed right after five warm-up launches ran 10 % slower
+    than after a few hundred more); a timed region should see the settled clock."""
+    import torch
+    t0 = time.perf_counter()
+    for _ in range(max(1, n)):
+        launch()
+    torch.cuda.synchronize()
+    per = (time.perf_counter() - t0) / max(1, n)
+    chunk = max(1, int(0.01 / max(per, 1e-6)))   # about 10 ms of launches between host waits
+    done = max(1, n)
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(chunk):
+            launch()
+        torch.cuda.synchronize()
+        done += chunk
+    return done
+
+
 def bench_workload(args, w, make_inputs):
     """Time one launch configuration of another workload; prints one JSON line."""
     import numpy as np
@@ -258,9 +281,7 @@ def bench_workload(args, w, make_inputs):
         if st != 0:
             raise ha.AttnError(st, "attn_fwd")
 
-    for _ in range(args.warmup):
-        launch()
-    torch.cuda.synchronize()
+    n_warm = warm_up(launch, args.warmup)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for e in evs:
@@ -287,7 +308,8 @@ def bench_workload(args, w, make_inputs):
     dtn = "bf16" if fmt == "bf16" else "fp8"
     print(json.dumps({
         "metric": f"attn fwd TFLOPS ({dtn}) at {w.name}", "value": round(tf, 2), "unit": "TFLOPS",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "warmup_launches": n_warm,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtn, "data": "synthetic",
         "config": {"workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Skv{w.Skv} D{w.D} "
                                f"{'causal' if causal else 'non-causal'}"
@@ -345,9 +367,7 @@ def bench_backward(args, w):
         if st != 0:
             raise ha.AttnError(st, "attn_bwd")
 
-    for _ in range(args.warmup):
-        launch()
-    torch.cuda.synchronize()
+    n_warm = warm_up(launch, args.warmup)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for e in evs:
@@ -373,7 +393,8 @@ def bench_backward(args, w):
                                     w, causal, args.cpu_seconds)
     print(json.dumps({
         "metric": f"attn bwd TFLOPS (bf16) at {w.name}", "value": round(tf, 2), "unit": "TFLOPS",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "warmup_launches": n_warm,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{w.name}: backward B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Skv{w.Skv} D{w.D} "
                                f"{'causal' if causal else 'non-causal'}, deterministic",
@@ -739,9 +760,7 @@ def main():
         if st != 0:
             raise ha.AttnError(st, "attn_fwd")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    n_warm = warm_up(step, args.warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -769,7 +788,7 @@ def main():
         tf = flops / t / 1e12
         return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
                 "frac": round(tf / PEAK_TFLOPS[dt], 4), "traffic": traffic.get(dt),
-                "kernel": f"attn_fwd_kernel<128,false,{'true' if dt == 'fp8' else 'false'},false,8,false>",
+                "kernel": f"attn_fwd_kernel<128,false,{'true' if dt == 'fp8' else 'false'},false,8,0>",
                 "mean_launch_ms": round(t * 1e3, 4),
                 "algorithmic_bytes": algorithmic_bytes(B, H, H, S, S, D, elt)}
 
@@ -788,6 +807,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_launches": n_warm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
