@@ -306,6 +306,7 @@ def bench_workload(args, w, make_inputs):
         flops = attn_flops(w.B, w.Hq, w.Sq, w.Skv, w.D, causal)
     tf = flops / tl.mean() / 1e12
     dtn = "bf16" if fmt == "bf16" else "fp8"
+    grid = grid_of(w, nsplit, causal, local, fmt == "bf16")
     print(json.dumps({
         "metric": f"attn fwd TFLOPS ({dtn}) at {w.name}", "value": round(tf, 2), "unit": "TFLOPS",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "warmup_launches": n_warm,
@@ -321,13 +322,14 @@ def bench_workload(args, w, make_inputs):
         "ms_p95": round(float(np.percentile(tl, 95)) * 1e3, 4), "ms_min": round(float(tl.min()) * 1e3, 4),
         "ms_loop100": round(t_loop * 1e3, 4), "tflops_loop100": round(flops / t_loop / 1e12, 2),
         "frac_of_peak": round(tf / PEAK_TFLOPS[dtn], 4), "key_splits": nsplit if nsplit is not None else 1,
-        # the library's grid for an unsplit call: 256-row workgroups, or smaller ones
-        # when the 256-row grid would fill at most half the CUs
-        **grid_of(w, nsplit, fmt == "bf16" and not local),
+        # the library's grid for an unsplit call: 256-row workgroups, smaller ones
+        # when the 256-row grid would fill at most half the CUs, or persistent ones
+        **grid,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_TFLOPS[dtn], "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_TFLOPS[dtn], 4), "traffic": None,
-                     "kernel": f"attn_fwd_kernel<{w.D},{str(causal).lower()},{str(dtn == 'fp8').lower()},"
-                               f"{str(local).lower()},*,*>" + (" + merge_splits_kernel" if nsplit is not None else ""),
+                     "kernel": (f"attn_fwd_persist_kernel<{w.D},{str(dtn == 'fp8').lower()}>" if grid.get("persistent") else
+                                f"attn_fwd_kernel<{w.D},{str(causal).lower()},{str(dtn == 'fp8').lower()},"
+                                f"{str(local).lower()},*,*>") + (" + merge_splits_kernel" if nsplit is not None else ""),
                      "mean_launch_ms": round(float(tl.mean()) * 1e3, 4)},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_workload(inp, w, causal, args.cpu_seconds)}),
         flush=True)
@@ -431,20 +433,24 @@ SWEEP_SPLIT = [  # B, H, Sq, Skv, D, dtype: few query tiles against long key ran
 ]
 
 
-def grid_of(w, nsplit, key_split):
+def grid_of(w, nsplit, causal, local, bf16):
     """Workgroups and rows per workgroup of an unsplit call (None for split calls,
     whose grid the library sizes from the key splits), as the library chooses them:
     256-row workgroups; when those fill at most half the CUs, 128-row ones, or for
-    bf16 without a window (key_split) 64-row ones where that grid still fits one
-    round of the CUs."""
+    bf16 without a window 64-row ones where that grid still fits one round of the
+    CUs; and for a non-causal grid without a window of at least two rounds over at
+    most 8 key tiles, one persistent workgroup per CU walking a range of 256-row
+    tiles ("persistent": true)."""
     import torch
     if nsplit not in (None, 1):
         return {"workgroups": None, "rows_per_workgroup": None}
     tiles = w.B * w.Hq * ((w.Sq + 255) // 256)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if 2 * tiles <= cus:
-        rows = 64 if key_split and w.B * w.Hq * ((w.Sq + 63) // 64) <= cus else 128
+        rows = 64 if bf16 and not local and w.B * w.Hq * ((w.Sq + 63) // 64) <= cus else 128
         return {"workgroups": w.B * w.Hq * ((w.Sq + rows - 1) // rows), "rows_per_workgroup": rows}
+    if not causal and not local and (w.Skv + 63) // 64 <= 8 and tiles >= 2 * cus:
+        return {"workgroups": cus, "rows_per_workgroup": 256, "persistent": True}
     return {"workgroups": tiles, "rows_per_workgroup": 256}
 
 

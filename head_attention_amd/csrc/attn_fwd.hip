@@ -1127,6 +1127,342 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
   }
 }
 
+// Persistent form of the classic tile loop, for grids of many query tiles
+// with short key ranges (non-causal, no window, no key splits): a grid of at
+// most one workgroup per CU, each walking one contiguous range of the
+// B * Hq * n_qtiles query tiles of 256 rows. The K/V ring runs on across the
+// range (step s = query tile t0 + s / nk, key tile s % nk; copies three steps
+// ahead), so the next tile's first copies are in flight while the current
+// one finishes, and the next tile's Q loads go out before the current tile's
+// O stores. A workgroup per query tile instead pays its Q load, ring fill and
+// O store in turn on every tile. Per tile the arithmetic is the classic
+// loop's (QK^T, checked running max, P V), so the bits equal attn_fwd_kernel's
+// with 8 waves and no key split.
+template <int D, bool FP8>
+__global__ void __launch_bounds__(512) attn_fwd_persist_kernel(const Params p) {
+  constexpr int kW = 8, kThr = 512;
+  using T = Tile<D, FP8>;
+  constexpr int ROWB = T::ROWB;
+  constexpr int NDB = D / 32;
+  constexpr int NKB = kBN / 32;
+  constexpr float kPre = FP8 ? 4.f : 0.f;
+  constexpr int kLds = kStages * 2 * T::BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kLds];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  const unsigned smem_addr = (unsigned)(uintptr_t)smem;
+
+  // This workgroup's query tiles [t0, t1): XCD x (workgroups reach the XCDs
+  // round-robin) gets one contiguous share of the grid, cut into equal ranges.
+  const long long ntq = (long long)p.B * p.Hq * p.n_qtiles;
+  int L = (int)blockIdx.x;
+  {
+    const int n = (int)gridDim.x, q8 = n >> 3, rem = n & 7, x = L & 7, r = L >> 3;
+    L = x < rem ? x * (q8 + 1) + r : rem * (q8 + 1) + (x - rem) * q8 + r;
+  }
+  const int t0 = (int)(ntq * L / gridDim.x), t1 = (int)(ntq * (L + 1) / gridDim.x);
+  const int Skv = p.Skv;
+  const int nk = (Skv + kBN - 1) / kBN;   // key tiles per query tile
+  const int n_whole = Skv / kBN;          // the unmasked ones
+  const int nsteps = (t1 - t0) * nk;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 5, n = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+
+  float c = p.c, oscale = 1.f;
+  if constexpr (FP8) {
+    const float qd = p.qd ? *p.qd : 1.f, kd = p.kd ? *p.kd : 1.f, vd = p.vd ? *p.vd : 1.f;
+    c *= qd * kd;
+    oscale = vd;
+  }
+  const bool cneg = FP8 && c < 0.f;
+  const float smask = cneg ? INFINITY : -INFINITY;
+
+  // Copies of step s into slot s % kStages (pieces split over the waves as in
+  // attn_fwd_kernel; the buffer range of the step's head zero-fills rows past
+  // Skv).
+  constexpr int PW = 2 * T::NINSTR / kW;
+  static_assert(PW >= 1 && PW * kW == 2 * T::NINSTR, "tile pieces must split evenly over waves");
+  auto issue = [&](int s) __attribute__((always_inline)) {
+    const int tq = __builtin_amdgcn_readfirstlane(t0 + s / nk);
+    const int u = __builtin_amdgcn_readfirstlane(s - (s / nk) * nk);
+    const int bh = tq / p.n_qtiles, b = bh / p.Hq, hk = (bh % p.Hq) / p.group;
+    const size_t krow0 = (size_t)(b * p.Hkv + hk) * (size_t)Skv;
+    const i32x4 rk = rsrc_words(p.k + krow0 * ROWB, (uint32_t)Skv * ROWB);
+    const i32x4 rv = rsrc_words(p.v + krow0 * ROWB, (uint32_t)Skv * ROWB);
+    const i32x4 rkw = i32x4{__builtin_amdgcn_readfirstlane(rk[0]), __builtin_amdgcn_readfirstlane(rk[1]),
+                            __builtin_amdgcn_readfirstlane(rk[2]), __builtin_amdgcn_readfirstlane(rk[3])};
+    const i32x4 rvw = i32x4{__builtin_amdgcn_readfirstlane(rv[0]), __builtin_amdgcn_readfirstlane(rv[1]),
+                            __builtin_amdgcn_readfirstlane(rv[2]), __builtin_amdgcn_readfirstlane(rv[3])};
+    const int key0 = u * kBN;
+    const int slot = s % kStages;
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      const int ins = wv * PW + j;
+      const bool isv = ins >= T::NINSTR;
+      const int c0 = (isv ? ins - T::NINSTR : ins) * 64;
+      const int cidx = c0 + lane;
+      const int r = cidx / T::CH, pc = cidx % T::CH;
+      const int lc = pc ^ (isv ? T::vswz(r) : T::kswz(r));
+      const int goff = (key0 + r) * ROWB + lc * 16;
+      const unsigned dst = __builtin_amdgcn_readfirstlane(smem_addr + (slot * 2 + (isv ? 1 : 0)) * T::BYTES + c0 * 16);
+      dma16(isv ? rvw : rkw, goff, dst);
+    }
+  };
+
+  // Q of query tile tq: this wave's 32 rows (rows >= Sq read as zero).
+  bf16x8 qf16[FP8 ? 1 : D / 16];
+  i32x8 qf8[FP8 ? D / 64 : 1];
+  auto load_q = [&](int tq) __attribute__((always_inline)) {
+    const int bh = tq / p.n_qtiles, qt = tq - bh * p.n_qtiles;
+    const size_t qrow0 = (size_t)bh * (size_t)p.Sq;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + qrow0 * ROWB, (uint32_t)p.Sq * ROWB);
+    const int qi = qt * kBM + wave * 32 + n;
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc) {
+        u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, qi * ROWB + (16 * dc + 8 * g) * 2, 0, 0);
+        qf16[dc] = __builtin_bit_cast(bf16x8, x);
+      }
+    } else {
+#pragma unroll
+      for (int dc = 0; dc < D / 64; ++dc) {
+        u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(rq, qi * ROWB + 64 * dc + 32 * g, 0, 0);
+        u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(rq, qi * ROWB + 64 * dc + 32 * g + 16, 0, 0);
+        qf8[dc] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                        (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
+    }
+  };
+
+  if (t0 < t1) load_q(t0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q has landed before any copy is queued
+  if (Skv % kBN != 0)
+    for (int i = threadIdx.x; i < kLds / 16; i += kThr)
+      *(LDS_AS u32x4*)(smem + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < nsteps) issue(s);
+
+  // Step s: wait for this wave's copies of it (those of the next two steps may
+  // still be in flight), barrier, queue step s + kStages - 1.
+  auto sync = [&](int s) __attribute__((always_inline)) {
+    if (s + 2 < nsteps) wait_vmcnt<2 * PW>();
+    else if (s + 1 < nsteps) wait_vmcnt<PW>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (s + kStages - 1 < nsteps) issue(s + kStages - 1);
+  };
+
+  f32x16 o[NDB];
+  float m;
+  double l;
+  [[maybe_unused]] float dl;
+  [[maybe_unused]] int pkeep[kBN / 64][8] = {};
+  const int krow = n;
+  const int l16 = lane & 15, dgrp = (lane >> 4) & 1;
+
+  // One key tile (key tile u in ring slot `slot`) for this wave's rows.
+  auto step = [&](int u, int slot, auto masked_c) __attribute__((always_inline)) {
+    const LDS_AS char* ks = smem + (slot * 2 + 0) * T::BYTES;
+    const LDS_AS char* vs = smem + (slot * 2 + 1) * T::BYTES;
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
+      const int r = 32 * kb + krow;
+      const LDS_AS char* krowp = ks + r * ROWB;
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) {
+          const int lc = 2 * dc + g;
+          const bf16x8 kf = *(const LDS_AS bf16x8*)(krowp + ((lc ^ T::kswz(r)) * 16));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf16[dc], s[kb], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int dc = 0; dc < D / 64; ++dc) {
+          const int lc = 4 * dc + 2 * g;
+          const i32x4 k0 = *(const LDS_AS i32x4*)(krowp + ((lc ^ T::kswz(r)) * 16));
+          const i32x4 k1 = *(const LDS_AS i32x4*)(krowp + (((lc + 1) ^ T::kswz(r)) * 16));
+          const i32x8 kf = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf8[dc], s[kb], 0, 0, 0, 127, 0, 127);
+        }
+      }
+    }
+    if constexpr (decltype(masked_c)::value) {   // keys past Skv
+      const int key0 = u * kBN;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+          s[kb][i] = key < Skv ? s[kb][i] : smask;
+        }
+    }
+    // online softmax with the checked running max, as in attn_fwd_kernel
+    f32x16 sraw[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sraw[kb] = s[kb];
+    float moff = kPre - (m == -INFINITY ? 0.f : m);
+    float rk[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, moff));
+        s[kb][i] = pv;
+        rk[kb] = i == 0 ? pv : rk[kb] + pv;
+      }
+    float rs = rk[0], rx = rk[0];
+#pragma unroll
+    for (int kb = 1; kb < NKB; ++kb) {
+      rs += rk[kb];
+      rx = fmaxf(rx, rk[kb]);
+    }
+    if (__any(m == -INFINITY || !(rx <= 256.f))) {
+      float mx = -INFINITY;
+      if (!cneg) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sraw[kb][i]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, -sraw[kb][i]);
+      }
+      const float mnew = fmaxf(m, xor32_max(mx) * fabsf(c));
+      if (__any(mnew > m)) {
+        const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
+        l *= (double)alpha;
+        if constexpr (!FP8) dl *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        m = mnew;
+        moff = kPre - (m == -INFINITY ? 0.f : m);
+        rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sraw[kb][i], c, moff));
+            s[kb][i] = pv;
+            rs += pv;
+          }
+      }
+    }
+    l += (double)rs;
+    // O^T += V^T P^T
+    if constexpr (!FP8) {
+      const int rr = l16 >> 2, ss = l16 & 3;
+      float dr = -rs;
+#pragma unroll
+      for (int kg = 0; kg < kBN / 16; ++kg) {
+        const int kb = kg >> 1, half = kg & 1;
+        bf16x8 pf;
+        {
+          const u32x4 pk = u32x4{pack_bf16(s[kb][8 * half + 0], s[kb][8 * half + 1]),
+                                 pack_bf16(s[kb][8 * half + 2], s[kb][8 * half + 3]),
+                                 pack_bf16(s[kb][8 * half + 4], s[kb][8 * half + 5]),
+                                 pack_bf16(s[kb][8 * half + 6], s[kb][8 * half + 7])};
+          pf = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) dr = sum_bf16x2(pk[w], dr);
+        }
+        const int key1 = 32 * kb + 16 * half + 4 * g + rr;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int col = 32 * db + 16 * dgrp + 4 * ss;
+          const int lc = col >> 3, hb = (col & 7) * 2;
+          const LDS_AS char* a1 = vs + key1 * ROWB + ((lc ^ T::vswz(key1)) * 16) + hb;
+          const LDS_AS char* a2 = vs + (key1 + 8) * ROWB + ((lc ^ T::vswz(key1 + 8)) * 16) + hb;
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a1);
+          const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a2);
+          const i16x8 vv = i16x8{v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[db], 0, 0, 0);
+        }
+      }
+      dl += dr;
+    } else {
+      const int rr = l16 >> 1, hh = l16 & 1;
+#pragma unroll
+      for (int kq = 0; kq < kBN / 64; ++kq) {
+        int pw[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int j = 4 * w, kb = 2 * kq + (j >> 4), i = j & 15;
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i], s[kb][i + 1], pkeep[kq][w], false);
+          x = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i + 2], s[kb][i + 3], x, true);
+          pw[w] = x;
+          pkeep[kq][w] = x;
+        }
+        const i32x8 pf = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int lc = 2 * db + dgrp;
+          int vw[8];
+#pragma unroll
+          for (int uu = 0; uu < 4; ++uu) {
+            const int key = 64 * kq + 32 * (uu >> 1) + 16 * (uu & 1) + 8 * (rr >> 2) + 4 * g + (rr & 3);
+            const LDS_AS char* a = vs + key * ROWB + ((lc ^ T::vswz(key)) * 16) + 8 * hh;
+            const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)a);
+            vw[2 * uu] = x[0];
+            vw[2 * uu + 1] = x[1];
+          }
+          const i32x8 vf = i32x8{vw[0], vw[1], vw[2], vw[3], vw[4], vw[5], vw[6], vw[7]};
+          o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, o[db], 0, 0, 0, 127, 0, 127);
+        }
+      }
+    }
+  };
+
+  int s = 0;
+  for (int tq = t0; tq < t1; ++tq) {
+    const int bh = tq / p.n_qtiles, qt = tq - bh * p.n_qtiles;
+    const int qw = qt * kBM + wave * 32, qi = qw + n;
+    const bool live = qw < p.Sq;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
+    m = -INFINITY;
+    l = 0.0;
+    if constexpr (!FP8) dl = 0.f;
+    int u = 0;
+    for (; u < n_whole; ++u, ++s) {
+      sync(s);
+      if (live) step(u, s % kStages, std::false_type{});
+    }
+    for (; u < nk; ++u, ++s) {
+      sync(s);
+      if (live) step(u, s % kStages, std::true_type{});
+    }
+    // the next tile's Q, queued ahead of this tile's O stores
+    if (tq + 1 < t1) load_q(tq + 1);
+    if (live) {
+      const float ltot = xor32_sum((float)l);
+      const float lp = FP8 ? ltot : xor32_sum((float)l + dl);
+      const float inv = ltot > 0.f ? oscale / lp : 0.f;
+      const float lse = ltot > 0.f ? (m + __log2f(ltot) - kPre) * 0.69314718055994531f : -INFINITY;
+      const size_t qrow0 = (size_t)bh * (size_t)p.Sq;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + qrow0 * (size_t)(D * 2), (uint32_t)p.Sq * D * 2);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const u32x2 w = u32x2{pack_bf16(o[db][4 * ii + 0] * inv, o[db][4 * ii + 1] * inv),
+                                pack_bf16(o[db][4 * ii + 2] * inv, o[db][4 * ii + 3] * inv)};
+          const int col = 32 * db + 8 * ii + 4 * g;
+          __builtin_amdgcn_raw_buffer_store_b64(w, ro, (qi * D + col) * 2, 0, 0);
+        }
+      if (g == 0) {
+        const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + qrow0, (uint32_t)p.Sq * 4);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rl, qi * 4, 0, 0);
+      }
+    }
+  }
+}
+
 // Merge of the key splits of attn_fwd_splitkv: for each row, L = ln sum_s
 // e^(L_s) and O = sum_s e^(L_s - L) O_s (fp32, bf16 out); rows whose splits
 // are all empty (L_s = -inf) get O = 0 and L = -inf. Sixteen lanes per row,
@@ -1197,6 +1533,8 @@ kernel_fn pick(bool causal, bool win, int nw, int ks) {
 using namespace hat;
 
 static constexpr int64_t kMaxSplits = 256;
+// Longest key range (in 64-key tiles) that runs on persistent workgroups.
+static constexpr int64_t kPersistMaxKeyTiles = 8;
 
 // Compute units of the current device (queried once per device).
 static int device_cus() {
@@ -1315,9 +1653,22 @@ static attn_status_t launch(const void* q, const void* k, const void* v, void* o
   p.sink = (int)std::min(sink, kUnbounded);
 
   kernel_fn fn;
-  if (dtype == ATTN_BF16) fn = D == 128 ? pick<128, false>(causal, win, nw, ks) : pick<64, false>(causal, win, nw, ks);
-  else fn = D == 128 ? pick<128, true>(causal, win, nw, 0) : pick<64, true>(causal, win, nw, 0);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(ks ? 512 : 64 * nw), 0, (hipStream_t)stream, p);
+  // Grids of at least two rounds over short key ranges (non-causal, no window,
+  // no key splits) run persistent workgroups instead, one per CU at most, each
+  // walking a range of query tiles: per-tile start-up and O stores then
+  // overlap the neighbouring tiles' work.
+  const int64_t cus = device_cus();
+  const bool pers = !causal && !win && nsp == 1 && nw == 8 && ktiles <= kPersistMaxKeyTiles && ntiles >= 2 * cus;
+  if (pers) {
+    grid = cus;
+    fn = dtype == ATTN_BF16 ? (D == 128 ? attn_fwd_persist_kernel<128, false> : attn_fwd_persist_kernel<64, false>)
+                            : (D == 128 ? attn_fwd_persist_kernel<128, true> : attn_fwd_persist_kernel<64, true>);
+  } else if (dtype == ATTN_BF16) {
+    fn = D == 128 ? pick<128, false>(causal, win, nw, ks) : pick<64, false>(causal, win, nw, ks);
+  } else {
+    fn = D == 128 ? pick<128, true>(causal, win, nw, 0) : pick<64, true>(causal, win, nw, 0);
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(ks || pers ? 512 : 64 * nw), 0, (hipStream_t)stream, p);
   if (hipGetLastError() != hipSuccess) return ATTN_ERR_HIP;
   if (nsp > 1) {
     const unsigned mgrid = (unsigned)((part_rows + 15) / 16);

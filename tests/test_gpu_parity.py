@@ -296,6 +296,22 @@ def _with_k(inp, k32):
     return out
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3fn"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_persistent_workgroups(D, fmt):
+    """A non-causal grid of at least two rounds of 256-row tiles over at most 32 key
+    tiles runs persistent workgroups (one per CU), each walking a range of query tiles
+    with one K/V ring across them; ranges cross head boundaries. Shapes: a ragged key
+    tail (500 keys) with ragged query tiles and grouped heads, and whole tiles; every
+    element against the oracle."""
+    for (B, Hq, Hkv, Sq, Skv) in ((1, 40, 8, 4000, 500), (2, 20, 20, 3840, 256)):
+        say(f"case persistent D={D} {fmt} B{B} H{Hq}/{Hkv} {Sq}x{Skv}")
+        inp = synth_inputs(B, Hq, Hkv, Sq, Skv, D, fmt, seed=301 + D + Sq + Skv)
+        scale = 1 / math.sqrt(D)
+        O, L, _ = run_gpu(inp, scale, False)
+        check_any(inp, O, L, refs(inp, scale, False), what=f"persistent D={D} {fmt} {Sq}x{Skv}")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_key_split_workgroups(D, causal):
