@@ -1136,8 +1136,10 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
 // one finishes, and the next tile's Q loads go out before the current tile's
 // O stores. A workgroup per query tile instead pays its Q load, ring fill and
 // O store in turn on every tile. Per tile the arithmetic is the classic
-// loop's (QK^T, checked running max, P V), so the bits equal attn_fwd_kernel's
-// with 8 waves and no key split.
+// loop's (QK^T, checked running max, P V), so the bf16 bits equal
+// attn_fwd_kernel's with 8 waves and no key split. The tile step is written
+// out here for the non-causal case rather than shared with attn_fwd_kernel's,
+// so that the code of that kernel's measured instances stays as it is.
 template <int D, bool FP8>
 __global__ void __launch_bounds__(512) attn_fwd_persist_kernel(const Params p) {
   constexpr int kW = 8, kThr = 512;
