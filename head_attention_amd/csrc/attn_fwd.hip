@@ -103,6 +103,16 @@ struct Params {
   int wl, wr, sink;
 };
 
+// The fp8 product of the page "F8 fmha ASM gfx950" (Technical Details: the
+// 32x32x64 fp8 MFMA for head dim 128): e4m3fn operands, fp32 accumulate, no
+// block scales. The builtin is the scaled form; with both scale operands 0 and
+// no op_sel the compiler emits the unscaled v_mfma_f32_32x32x64_f8f6f4, a
+// shorter instruction that holds no VGPR for a scale (the scaled form with
+// unit scales issued as the longer encoding and pinned a register to 127).
+__device__ __forceinline__ f32x16 mfma_e4m3(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // LDS layout of one K or V tile: kBN rows of ROWB bytes, 16-byte chunks permuted
 // within a row by an XOR swizzle so that the MFMA operand reads hit distinct banks.
 template <int D, bool FP8>
@@ -425,7 +435,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
           const i32x4 k0 = *(const LDS_AS i32x4*)(krowp + ((lc ^ T::kswz(r)) * 16));
           const i32x4 k1 = *(const LDS_AS i32x4*)(krowp + (((lc + 1) ^ T::kswz(r)) * 16));
           const i32x8 kf = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-          s[kk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf8[dc], s[kk], 0, 0, 0, 127, 0, 127);
+          s[kk] = mfma_e4m3(kf, qf8[dc], s[kk]);
         }
       }
     }
@@ -571,7 +581,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
             vw[2 * u + 1] = x[1];
           }
           const i32x8 vf = i32x8{vw[0], vw[1], vw[2], vw[3], vw[4], vw[5], vw[6], vw[7]};
-          o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, o[db], 0, 0, 0, 127, 0, 127);
+          o[db] = mfma_e4m3(vf, pf, o[db]);
         }
       }
     }
@@ -695,7 +705,7 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       return i32x8{vw[0], vw[1], vw[2], vw[3], vw[4], vw[5], vw[6], vw[7]};
     };
     auto mfma8 = [](i32x8 a, i32x8 b, f32x16 c) __attribute__((always_inline)) {
-      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+      return mfma_e4m3(a, b, c);
     };
     // S(next) = K Q^T and O += V^T P(prev), MFMAs alternating between the two
     // products; do_qk / do_pv drop either (edge iterations).
@@ -1288,7 +1298,7 @@ __global__ void __launch_bounds__(512) attn_fwd_persist_kernel(const Params p) {
           const i32x4 k0 = *(const LDS_AS i32x4*)(krowp + ((lc ^ T::kswz(r)) * 16));
           const i32x4 k1 = *(const LDS_AS i32x4*)(krowp + (((lc + 1) ^ T::kswz(r)) * 16));
           const i32x8 kf = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf8[dc], s[kb], 0, 0, 0, 127, 0, 127);
+          s[kb] = mfma_e4m3(kf, qf8[dc], s[kb]);
         }
       }
     }
@@ -1414,7 +1424,7 @@ __global__ void __launch_bounds__(512) attn_fwd_persist_kernel(const Params p) {
             vw[2 * uu + 1] = x[1];
           }
           const i32x8 vf = i32x8{vw[0], vw[1], vw[2], vw[3], vw[4], vw[5], vw[6], vw[7]};
-          o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, o[db], 0, 0, 0, 127, 0, 127);
+          o[db] = mfma_e4m3(vf, pf, o[db]);
         }
       }
     }
