@@ -766,17 +766,24 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       float rs, rx;
       expo(moff, rs, rx);
       if constexpr (decltype(sched_c)::value) {
-        // Interleave: the 8 MFMAs of mma() one by one, each followed by its
-        // share of the softmax VALU work and the LDS operand reads (2 or 4) of
-        // the MFMA two places later.
-#define HAT_SLOT(nds, nv)                                \
+        // Interleave: the 8 MFMAs of mma() one by one, each followed by the
+        // LDS operand reads (2 or 4) of the MFMA two places later and its share
+        // of the softmax: 10 VALU and 4 exp2 (v_exp_f32 is a transcendental,
+        // mask 0x400, which the VALU mask 0x002 does not take; counted apart
+        // they stay spread over the slots instead of gathering in the first
+        // ones). The first MFMA waits on the K reads queued at the top of the
+        // iteration, so 12 VALU and 4 exp2 go ahead of it; the last two slots
+        // take what is left (6 + 2 and 4 + 2 of the 82 + 32).
+#define HAT_SLOT(nds, nv, nt)                            \
   __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     \
   __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);   \
-  __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);    \
+  __builtin_amdgcn_sched_group_barrier(0x400, nt, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        HAT_SLOT(2, 14) HAT_SLOT(4, 14) HAT_SLOT(2, 14) HAT_SLOT(4, 14)
-        HAT_SLOT(2, 14) HAT_SLOT(4, 14) HAT_SLOT(0, 14) HAT_SLOT(0, 14)
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);
+        HAT_SLOT(2, 10, 4) HAT_SLOT(4, 10, 4) HAT_SLOT(2, 10, 4) HAT_SLOT(4, 10, 4)
+        HAT_SLOT(2, 10, 4) HAT_SLOT(4, 10, 4) HAT_SLOT(0, 6, 2) HAT_SLOT(0, 4, 2)
 #undef HAT_SLOT
       }
       // In steady iterations tile 0 has given every row a finite m, so only
