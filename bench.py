@@ -461,7 +461,8 @@ def mfma_ceiling(dev):
     with HIP events over launches of ~15 ms, after the attention timing; and under
     ``with_softmax`` the same MFMAs each followed by its share of the attention tile's
     softmax VALU instructions (the best an attention loop with that instruction mix can
-    do here). Also the dense peak from the device's CU count and peak clock. None when
+    do here); under ``valu_rates`` the issue cost of v_exp_f32 and v_fma_f32 alone and
+    mixed. Also the dense peak from the device's CU count and peak clock. None when
     the probe is not built."""
     import ctypes
     import numpy as np
@@ -513,6 +514,35 @@ def mfma_ceiling(dev):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e-3)
         into[name] = round(nblocks * 4 * iters * 8 * fl / float(np.median(ts)) / 1e12, 1)
+    # VALU issue rates of the softmax's exp2 and fma, alone and mixed (valu_rate_kernel):
+    # time per wave-instruction on one SIMD, eight waves per SIMD.
+    L.valu_rate_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    L.valu_rate_probe_launch.restype = ctypes.c_int
+    vblocks, viters = 8 * cus.value, 16384
+    vout = torch.empty(vblocks * 256, device=dev)
+    vt = {}
+    for kind, name in ((0, "exp2"), (1, "fma"), (2, "exp2+fma")):
+        def vcall():
+            if L.valu_rate_probe_launch(kind, vblocks, viters, vout.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError("VALU rate probe launch failed")
+        vcall()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            vcall()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        vt[name] = float(np.median(ts)) / (viters * 8 * 8) * 1e9   # ns per wave-instruction (of each form) per SIMD
+    res["valu_rates"] = {
+        "kernel": "valu_rate_kernel (libmfma_probe.so): 8 independent v_exp_f32 or v_fma_f32 chains per lane, "
+                  "8 waves per SIMD; ns per wave-instruction on one SIMD",
+        "exp2_ns": round(vt["exp2"], 3), "fma_ns": round(vt["fma"], 3),
+        "exp2_over_fma": round(vt["exp2"] / vt["fma"], 2),
+        "mixed_over_sum": round(vt["exp2+fma"] / (vt["exp2"] + vt["fma"]), 3)}
     mhz = clk.value / 1e3
     res["device"] = {"cus": cus.value, "peak_clock_mhz": mhz,
                      "dense_peak_bf16": round(cus.value * mhz * 1e6 * 4096 / 1e12, 1),

@@ -1,9 +1,10 @@
 // MFMA throughput probes for gfx950 (MI355X), a measurement aid for the
 // benchmark, not part of the attention boundary. The first shows what the
 // matrix cores sustain on this device under the attention kernels' own MFMA
-// forms (bf16 32x32x16 and fp8 32x32x64 with unit scales) when nothing else
-// runs; the second (mfma_softmax_kernel, below) adds the attention tile's own
-// softmax VALU instructions between the MFMAs.
+// forms (bf16 32x32x16 and the unscaled fp8 32x32x64) when nothing else runs;
+// the second (mfma_softmax_kernel, below) adds the attention tile's own
+// softmax VALU instructions between the MFMAs; the third (valu_rate_kernel)
+// times the softmax's two main VALU forms, exp2 and fma, alone and mixed.
 // Every wave issues only MFMAs on register operands loaded once from a buffer
 // of random values, rotating over eight A and eight B fragments so that the
 // operand data changes from one MFMA to the next as it does in attention (the
@@ -25,6 +26,12 @@ using hat::i32x4;
 using hat::i32x8;
 
 constexpr int kFrags = 8;   // operand fragments per matrix, rotated
+
+// The unscaled fp8 MFMA: the scaled builtin with zero scale operands, which the
+// compiler emits as v_mfma_f32_32x32x64_f8f6f4 (the attention kernels' form).
+__device__ __forceinline__ f32x16 mfma_e4m3(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
 
 template <bool FP8>
 __global__ void __launch_bounds__(256) mfma_ceiling_kernel(const int* __restrict__ src, float* __restrict__ out,
@@ -58,8 +65,7 @@ __global__ void __launch_bounds__(256) mfma_ceiling_kernel(const int* __restrict
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int j = 0; j < kFrags; ++j)
-        acc[j & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j], b[(3 * j + 1) & (kFrags - 1)], acc[j & 3],
-                                                                     0, 0, 0, 127, 0, 127);
+        acc[j & 3] = mfma_e4m3(a[j], b[(3 * j + 1) & (kFrags - 1)], acc[j & 3]);
     }
   }
   float s = 0.f;
@@ -109,8 +115,7 @@ __global__ void __launch_bounds__(256) mfma_softmax_kernel(const int* __restrict
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int j = 0; j < kFrags; ++j) {
-        acc[j & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j], b[(3 * j + 1) & (kFrags - 1)], acc[j & 3],
-                                                                     0, 0, 0, 127, 0, 127);
+        acc[j & 3] = mfma_e4m3(a[j], b[(3 * j + 1) & (kFrags - 1)], acc[j & 3]);
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j][e], c, d));
@@ -161,6 +166,32 @@ __global__ void __launch_bounds__(256) mfma_softmax_kernel(const int* __restrict
   out[gw * 64 + lane] = s;   // keeps the MFMAs and the VALU work live
 }
 
+// VALU issue rates of the softmax's main forms: KIND 0 issues only v_exp_f32
+// (eight independent chains x <- exp2(-x), which stay in (0, 1)), KIND 1 only
+// v_fma_f32 (eight chains x <- 0.999 x + 0.001), KIND 2 both, one fma after
+// each exp2. Workgroups of 4 waves; eight workgroups per compute unit give
+// each SIMD eight waves, so that latency never limits the issue rate.
+template <int KIND>
+__global__ void __launch_bounds__(256) valu_rate_kernel(float* __restrict__ out, int iters) {
+  float e[8], f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    e[i] = 0.5f + 0.01f * i + 1e-6f * threadIdx.x;
+    f[i] = 0.5f + 0.02f * i + 1e-6f * threadIdx.x;
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (KIND != 1) e[i] = __builtin_amdgcn_exp2f(-e[i]);
+      if (KIND != 0) f[i] = __builtin_fmaf(f[i], 0.999f, 0.001f);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += e[i] + f[i];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 }  // namespace probe
 
 // Launches nblocks workgroups of 4 waves on `stream`, each wave issuing
@@ -193,6 +224,22 @@ extern "C" int mfma_softmax_probe_launch(int fp8, int64_t nblocks, int iters, co
   else
     hipLaunchKernelGGL(probe::mfma_softmax_kernel<false>, grid, block, 0, (hipStream_t)stream, (const int*)src,
                        (float*)out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Launches nblocks workgroups of 4 waves of valu_rate_kernel<kind> (kind 0:
+// exp2 only, 1: fma only, 2: both) on `stream`, each wave issuing iters * 8
+// instructions of each form it runs; out: device buffer of nblocks * 256
+// floats. Returns 0, 1 for bad arguments, 2 when the launch fails.
+extern "C" int valu_rate_probe_launch(int kind, int64_t nblocks, int iters, void* out, void* stream) {
+  if (kind < 0 || kind > 2 || nblocks <= 0 || nblocks >= (int64_t)1 << 31 || iters <= 0 || !out) return 1;
+  const dim3 grid((unsigned)nblocks), block(256);
+  if (kind == 0)
+    hipLaunchKernelGGL(probe::valu_rate_kernel<0>, grid, block, 0, (hipStream_t)stream, (float*)out, iters);
+  else if (kind == 1)
+    hipLaunchKernelGGL(probe::valu_rate_kernel<1>, grid, block, 0, (hipStream_t)stream, (float*)out, iters);
+  else
+    hipLaunchKernelGGL(probe::valu_rate_kernel<2>, grid, block, 0, (hipStream_t)stream, (float*)out, iters);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
