@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_mfma_probe_library_loads_and_refuses_bad_arguments():
     """The benchmark's MFMA probes (a measurement aid beside the attention library)
-    export their three entry points and reject bad arguments without launching."""
+    export their four entry points and reject bad arguments without launching."""
     import ctypes
     path = os.path.join(ROOT, "head_attention_amd", "libmfma_probe.so")
     if not os.path.exists(path):
@@ -58,6 +58,13 @@ def test_mfma_probe_library_loads_and_refuses_bad_arguments():
     assert P.mfma_softmax_probe_launch(1, 0, 10, 1 << 20, 1 << 20, None) == 1
     assert P.mfma_softmax_probe_launch(0, 4, 0, 1 << 20, 1 << 20, None) == 1
     assert P.mfma_softmax_probe_launch(1, 4, 10, 1 << 20, None, None) == 1   # no output buffer
+    P.valu_rate_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.valu_rate_probe_launch.restype = ctypes.c_int
+    assert P.valu_rate_probe_launch(3, 4, 10, 1 << 20, None) == 1             # no such kind
+    assert P.valu_rate_probe_launch(-1, 4, 10, 1 << 20, None) == 1
+    assert P.valu_rate_probe_launch(0, 0, 10, 1 << 20, None) == 1             # no workgroups
+    assert P.valu_rate_probe_launch(1, 4, 0, 1 << 20, None) == 1              # no iterations
+    assert P.valu_rate_probe_launch(2, 4, 10, None, None) == 1                # no output buffer
 
 
 def test_status_strings(L):
