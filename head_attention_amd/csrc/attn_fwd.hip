@@ -440,6 +440,20 @@ __global__ void __launch_bounds__(64 * NW) attn_fwd_kernel(const Params p) {
       }
     }
 
+    if constexpr (!FP8) {
+      // K operand reads four MFMAs ahead of their use, in a region of their
+      // own, instead of each read right before its MFMA.
+      constexpr int NM = NB * (D / 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NM - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
     // ---- mask: keys past Skv, and (causal) keys after the query ----
     if constexpr (decltype(masked_c)::value) {
       const int key0 = t * kBN;
