@@ -258,12 +258,23 @@ __global__ void __launch_bounds__(kThreads) attn_bwd_dq_kernel(const Params p) {
     for (int kb = 0; kb < NKB; ++kb) {
       // S^T = K Q^T and dP^T = V dO^T for 32 keys
       f32x16 s = f32x16{}, dp = f32x16{};
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc) {
         const int off = (rb ^ (dc << 5)) + 32 * kb * ROWB;
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(ks + off), qf[dc], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(vs + off), df[dc], dp, 0, 0, 0);
       }
+      // operand reads four MFMAs ahead of their use, in a region of their own
+      // (each read right before its MFMA otherwise)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * (D / 16) - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (decltype(masked_c)::value) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
